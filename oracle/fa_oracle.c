@@ -1,0 +1,298 @@
+/*
+ * fa_oracle.c -- the fp64 CPU oracle for exact attention and its split-KV
+ * (partial output + log-sum-exp) combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the test suite, the package smoke check and the CPU
+ * baseline leg of the benchmark use it.  It shares no code, header, table or
+ * helper with the HIP kernels.
+ *
+ * What it computes (sources, by page and section):
+ *
+ *  - "FlashAttention-3 vs Triton Kernels: Warp-Specialization on GPUs"
+ *    (dailyaiworld.com), introduction: FlashAttention computes ordinary
+ *    softmax attention; its tiling only avoids storing the N x N score
+ *    matrix in HBM.  The plain definition is therefore the oracle:
+ *        s_ij = scale * <q_i, k_j>
+ *        O_i  = sum_j softmax_j(s_i.) v_j
+ *        lse_i = log sum_j exp(s_ij)
+ *    over the keys j visible to query i.
+ *  - Same page, "Benchmarking Triton vs FlashAttention-3 Kernels": tensors
+ *    are laid out (batch, heads, seq_len, head_dim) and the benchmarked call
+ *    is the non-causal default, whose scale is 1/sqrt(head_dim).
+ *  - post.smzdm.com digest on Triton warp specialisation, section 5
+ *    (attention cannot be split like a GEMM): partial attention outputs over
+ *    disjoint key shards cannot be added, because each shard has its own
+ *    softmax denominator; each shard must carry its log-sum-exp, and the
+ *    combine re-normalises the partial outputs with it.  oracle_combine()
+ *    is that re-normalisation written out.
+ *
+ * Readings where the pages are silent (each one is listed in the design
+ * notes): causal means key j is visible to query i iff j <= i; the
+ * grouped-query map sends query head hq to key/value head hq / (Hq/Hkv);
+ * lse is the natural log; a query with no visible key gets O = 0 and
+ * lse = -inf.
+ *
+ * Precision: inputs are the exact 16-bit values the GPU consumes (bf16 or
+ * fp16 bit patterns), widened exactly to double; everything after that is
+ * plain fp64 in a two-pass (max, then exp-sum) softmax.
+ *
+ * ORACLE_MUTANT (compile-time, default 0) plants one deliberate mistake per
+ * value.  Only the test that proves the pins can catch a wrong oracle builds
+ * those variants; the normal build never defines it.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+#define ORACLE_BF16 0
+#define ORACLE_FP16 1
+
+/* Exact widening of one 16-bit storage value to double. */
+double oracle_widen(uint16_t bits, int dtype)
+{
+    if (dtype == ORACLE_BF16) {
+        /* bfloat16 is the top half of an IEEE binary32. */
+#if ORACLE_MUTANT == 11
+        uint32_t w = (uint32_t)bits << 15;
+#else
+        uint32_t w = (uint32_t)bits << 16;
+#endif
+        float f;
+        memcpy(&f, &w, sizeof f);
+        return (double)f;
+    }
+    /* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+    int sign = (bits >> 15) & 1;
+    int e = (bits >> 10) & 0x1f;
+    int frac = bits & 0x3ff;
+#if ORACLE_MUTANT == 8
+    const int bias = 14;
+#else
+    const int bias = 15;
+#endif
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)frac, 1 - bias - 10);          /* subnormal */
+    else if (e == 31)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(1024 + frac), e - bias - 10);
+    return sign ? -mag : mag;
+}
+
+static int kv_head_of(long hq, long Hq, long Hkv)
+{
+#if ORACLE_MUTANT == 5
+    (void)Hq;
+    return (int)(hq % Hkv);
+#else
+    long group = Hq / Hkv;          /* query heads per key/value head */
+    return (int)(hq / group);
+#endif
+}
+
+static int key_visible(long j, long i, int causal)
+{
+    if (!causal)
+        return 1;
+#if ORACLE_MUTANT == 2
+    return j < i;
+#else
+    return j <= i;
+#endif
+}
+
+/*
+ * Attention for an explicit list of query rows, restricted to keys in
+ * [klo, khi) (the full key set is [0, Nk)).
+ *
+ *   q     [B, Hq,  Nq, d]  16-bit bit patterns, d fastest
+ *   k, v  [B, Hkv, Nk, d]  16-bit bit patterns
+ *   rows  nrows triples (b, hq, i)
+ *   out_o [nrows, d] double, out_lse [nrows] double
+ *
+ * Returns 0, or -1 on a bad argument (nothing written).
+ */
+int oracle_attention_rows(const uint16_t *q, const uint16_t *k,
+                          const uint16_t *v, int dtype, long B, long Hq,
+                          long Hkv, long Nq, long Nk, long d, int causal,
+                          double scale, long klo, long khi, const long *rows,
+                          long nrows, double *out_o, double *out_lse)
+{
+    if (!q || !k || !v || !rows || !out_o || !out_lse)
+        return -1;
+    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 0 || Nk < 0 || d < 1)
+        return -1;
+    if (klo < 0) klo = 0;
+    if (khi > Nk) khi = Nk;
+    for (long r = 0; r < nrows; ++r) {
+        long b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        if (b < 0 || b >= B || h < 0 || h >= Hq || i < 0 || i >= Nq)
+            return -1;
+    }
+
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        double *qd = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!s || !qd) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long r = 0; r < nrows; ++r) {
+            if (!s || !qd)
+                continue;
+            long b = rows[3 * r], hq = rows[3 * r + 1], i = rows[3 * r + 2];
+            long g = kv_head_of(hq, Hq, Hkv);
+            const uint16_t *qi = q + ((b * Hq + hq) * Nq + i) * d;
+            const uint16_t *kb = k + (b * Hkv + g) * Nk * d;
+            const uint16_t *vb = v + (b * Hkv + g) * Nk * d;
+#if ORACLE_MUTANT == 4
+            kb = v + (b * Hkv + g) * Nk * d;
+#endif
+            double *o = out_o + r * d;
+            for (long c = 0; c < d; ++c)
+                qd[c] = oracle_widen(qi[c], dtype);
+
+            /* pass 1: scores of the visible keys and their maximum */
+            double m = -INFINITY;
+            long nvis = 0;
+            for (long j = klo; j < khi; ++j) {
+                if (!key_visible(j, i, causal))
+                    continue;
+                const uint16_t *kj = kb + j * d;
+                double dot = 0.0;
+#if ORACLE_MUTANT == 10
+                for (long c = 0; c + 1 < d; ++c)
+#else
+                for (long c = 0; c < d; ++c)
+#endif
+                    dot += qd[c] * oracle_widen(kj[c], dtype);
+#if ORACLE_MUTANT == 1
+                s[j] = -scale * dot;
+#else
+                s[j] = scale * dot;
+#endif
+                if (s[j] > m)
+                    m = s[j];
+                ++nvis;
+            }
+            for (long c = 0; c < d; ++c)
+                o[c] = 0.0;
+            if (nvis == 0) {
+                out_lse[r] = -INFINITY;
+                continue;
+            }
+
+            /* pass 2: l = sum exp(s - m), O = sum exp(s - m) v / l */
+            double l = 0.0;
+            for (long j = klo; j < khi; ++j) {
+                if (!key_visible(j, i, causal))
+                    continue;
+                double p = exp(s[j] - m);
+                l += p;
+#if ORACLE_MUTANT == 9
+                const uint16_t *vj = vb + ((j + 1) % Nk) * d;
+#else
+                const uint16_t *vj = vb + j * d;
+#endif
+                for (long c = 0; c < d; ++c)
+                    o[c] += p * oracle_widen(vj[c], dtype);
+            }
+#if ORACLE_MUTANT != 6
+            for (long c = 0; c < d; ++c)
+                o[c] /= l;
+#endif
+#if ORACLE_MUTANT == 3
+            out_lse[r] = log(l);
+#else
+            out_lse[r] = m + log(l);
+#endif
+        }
+        free(s);
+        free(qd);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Combine nsplit partial results of one query row, each the attention over a
+ * disjoint key shard, into the attention over the union of the shards
+ * (smzdm digest, section 5: every shard carries its log-sum-exp and the
+ * combine re-normalises with it):
+ *     lse = log sum_s exp(lse_s)          (computed as M + log sum exp(lse_s - M))
+ *     O   = sum_s exp(lse_s - lse) O_s
+ * A shard with lse_s = -inf (no visible key) has weight zero.
+ *
+ *   part_o [nsplit, d], part_lse [nsplit]  ->  o [d], *lse
+ */
+void oracle_combine(const double *part_o, const double *part_lse, long nsplit,
+                    long d, double *o, double *lse)
+{
+    double M = -INFINITY;
+    for (long s = 0; s < nsplit; ++s)
+        if (part_lse[s] > M)
+            M = part_lse[s];
+    for (long c = 0; c < d; ++c)
+        o[c] = 0.0;
+    if (M == -INFINITY) {
+        *lse = -INFINITY;
+        return;
+    }
+    double wsum = 0.0;
+    for (long s = 0; s < nsplit; ++s)
+        wsum += exp(part_lse[s] - M);
+#if ORACLE_MUTANT == 12
+    double L = M;
+#else
+    double L = M + log(wsum);
+#endif
+    for (long s = 0; s < nsplit; ++s) {
+#if ORACLE_MUTANT == 7
+        double w = 1.0;
+#else
+        double w = exp(part_lse[s] - L);
+#endif
+        for (long c = 0; c < d; ++c)
+            o[c] += w * part_o[s * d + c];
+    }
+    *lse = L;
+}
+
+/*
+ * Single-token decode against a key/value cache, the unsplit definition:
+ *   q [B, Hq, d], kcache, vcache [B, Hkv, L, d]  ->  o [B, Hq, d], lse [B, Hq]
+ * All L cached keys are visible; scale is 1/sqrt(d) (the benchmarked
+ * default on the dailyaiworld page).
+ */
+int oracle_decode(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
+                  int dtype, long B, long Hq, long Hkv, long L, long d,
+                  double *out_o, double *out_lse)
+{
+    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || L < 0 || d < 1)
+        return -1;
+    long n = B * Hq;
+    long *rows = (long *)malloc(sizeof(long) * 3 * (size_t)(n > 0 ? n : 1));
+    if (!rows)
+        return -1;
+    for (long b = 0; b < B; ++b)
+        for (long h = 0; h < Hq; ++h) {
+            long r = b * Hq + h;
+            rows[3 * r] = b;
+            rows[3 * r + 1] = h;
+            rows[3 * r + 2] = 0;
+        }
+    int rc = oracle_attention_rows(q, kc, vc, dtype, B, Hq, Hkv, 1, L, d, 0,
+                                   1.0 / sqrt((double)d), 0, L, rows, n,
+                                   out_o, out_lse);
+    free(rows);
+    return rc;
+}

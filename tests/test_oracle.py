@@ -1,0 +1,329 @@
+"""Pins for the fp64 oracle: each checks it against something other than
+itself (closed forms, hand-worked examples, invariants, a library routine,
+pure-Python brute force).  A final test builds deliberately broken oracles
+and checks that every planted mistake is caught by at least one pin.
+
+Runs on the CPU only.
+"""
+import math
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+import torch
+
+from flashattention_attention_fa_amd import synth
+from oracle import oracle as oracle_mod
+
+GOLDEN = Path(__file__).parent / "golden" / "worked_examples.txt"
+
+
+def bits_of(values, dtype):
+    t = torch.as_tensor(np.array(values, dtype=np.float32)).to(synth.TORCH_DTYPES[dtype])
+    return synth.to_bits(t)
+
+
+def widened(bits, dtype):
+    """Library widening (torch), used only to build expected values."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(synth.TORCH_DTYPES[dtype])
+    return t.to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------------------
+# pins: functions of an Oracle instance, so the mutation test can reuse them
+# ---------------------------------------------------------------------------
+
+def pin_widen_all_patterns(orc):
+    """Every bf16 and fp16 bit pattern widens to the value torch/numpy give."""
+    allbits = np.arange(65536, dtype=np.uint16)
+    for dtype in ("bf16", "fp16"):
+        ref = widened(allbits, dtype)
+        sample = np.concatenate([allbits[:2048], allbits[0x3000:0x4400], allbits[0x7b00:0x8400],
+                                 allbits[0xb000:0xc400], allbits[-256:]])
+        for b in sample[::7]:
+            got = orc.widen(int(b), dtype)
+            want = ref[int(b)]
+            if math.isnan(want):
+                assert math.isnan(got), (dtype, hex(b))
+            else:
+                assert got == want, (dtype, hex(b), got, want)
+
+
+def _parse_golden():
+    blocks, cur = [], None
+    for line in GOLDEN.read_text().splitlines():
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, _, val = line.partition(":")
+        val = val.strip()
+        if key == "example":
+            cur = {"name": val, "o": {}, "lse": {}}
+            blocks.append(cur)
+        elif key in ("q", "k", "v"):
+            cur[key] = [[float(x) for x in row.split()] for row in val.split("|")]
+        elif key in ("scale",):
+            cur[key] = float(val)
+        elif key == "causal":
+            cur[key] = bool(int(val))
+        else:
+            m = re.fullmatch(r"expect_(o|lse)\[(\d+)\]", key)
+            assert m, key
+            exprs = [e.strip() for e in val.split(";")]
+            env = {"math": math, "__builtins__": {}}
+            vals = [eval(e, env) for e in exprs]  # closed forms over math.* only
+            cur[m.group(1)][int(m.group(2))] = vals
+    return blocks
+
+
+def pin_worked_examples(orc):
+    for ex in _parse_golden():
+        for dtype in ("bf16", "fp16"):
+            q = bits_of(ex["q"], dtype)[None, None]
+            k = bits_of(ex["k"], dtype)[None, None]
+            v = bits_of(ex["v"], dtype)[None, None]
+            o, lse = orc.attention(q, k, v, dtype, ex["causal"], ex["scale"])
+            for i, want in ex["o"].items():
+                np.testing.assert_allclose(o[0, 0, i], want, rtol=1e-13, atol=1e-13,
+                                           err_msg=ex["name"])
+            for i, want in ex["lse"].items():
+                np.testing.assert_allclose(lse[0, 0, i], want[0], rtol=1e-13, atol=1e-13,
+                                           err_msg=ex["name"])
+
+
+def pin_single_key(orc):
+    """One key: softmax over a single element is 1, so O = v0 and
+    lse = scale * <q, k0>."""
+    for dtype in ("bf16", "fp16"):
+        q, k, v = synth.fwd_inputs(2, 3, 1, 64, dtype, seed=11)
+        qb, kb, vb = synth.to_bits(q), synth.to_bits(k), synth.to_bits(v)
+        scale = 0.125
+        o, lse = orc.attention(qb, kb, vb, dtype, False, scale)
+        np.testing.assert_array_equal(o[:, :, 0], widened(vb, dtype)[:, :, 0])
+        dots = np.einsum("bhd,bhd->bh", widened(qb, dtype)[:, :, 0], widened(kb, dtype)[:, :, 0])
+        np.testing.assert_allclose(lse[:, :, 0], scale * dots, rtol=1e-12, atol=1e-12)
+
+
+def pin_causal_row0(orc):
+    """Causal: query 0 sees only key 0, on any length."""
+    q, k, v = synth.fwd_inputs(1, 2, 37, 32, "bf16", seed=12)
+    qb, kb, vb = synth.to_bits(q), synth.to_bits(k), synth.to_bits(v)
+    o, lse = orc.attention(qb, kb, vb, "bf16", True, 0.3)
+    np.testing.assert_array_equal(o[:, :, 0], widened(vb, "bf16")[:, :, 0])
+    dots = np.einsum("bhd,bhd->bh", widened(qb, "bf16")[:, :, 0], widened(kb, "bf16")[:, :, 0])
+    np.testing.assert_allclose(lse[:, :, 0], 0.3 * dots, rtol=1e-12, atol=1e-12)
+
+
+def pin_uniform_when_q_zero(orc):
+    """Q = 0 makes every visible score 0: O_i is the mean of the visible V
+    rows and lse_i = log(#visible) (log N non-causal, log(i+1) causal)."""
+    N, d = 45, 16
+    _, k, v = synth.fwd_inputs(2, 2, N, d, "fp16", seed=13)
+    qb = np.zeros((2, 2, N, d), np.uint16)
+    kb, vb = synth.to_bits(k), synth.to_bits(v)
+    vw = widened(vb, "fp16")
+    for causal in (False, True):
+        o, lse = orc.attention(qb, kb, vb, "fp16", causal, 0.7)
+        for i in (0, 1, 17, N - 1):
+            n = i + 1 if causal else N
+            np.testing.assert_allclose(o[:, :, i], vw[:, :, :n].mean(axis=2), rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(lse[:, :, i], math.log(n), rtol=1e-13, atol=1e-13)
+
+
+def pin_constant_v(orc):
+    """Every V row equal to c gives O = c whatever the weights."""
+    q, k, _ = synth.fwd_inputs(1, 2, 50, 8, "bf16", seed=14)
+    c = np.array([1.5, -2.0, 0.25, 3.0, 0.0, -0.5, 8.0, 1.0], np.float32)
+    vb = bits_of(np.broadcast_to(c, (1, 2, 50, 8)), "bf16")
+    for causal in (False, True):
+        o, _ = orc.attention(synth.to_bits(q), synth.to_bits(k), vb, "bf16", causal, 0.9)
+        np.testing.assert_allclose(o, np.broadcast_to(c, o.shape), rtol=1e-12, atol=1e-12)
+
+
+def pin_weights_sum_to_one(orc):
+    """With V = identity (d = N), row i of O is the softmax weight vector of
+    query i: non-negative, summing to 1, zero on keys a causal mask hides."""
+    N = 24
+    q, k, _ = synth.fwd_inputs(1, 1, N, N, "bf16", seed=15)
+    vb = bits_of(np.eye(N)[None, None], "bf16")
+    for causal in (False, True):
+        o, _ = orc.attention(synth.to_bits(q), synth.to_bits(k), vb, "bf16", causal, 0.5)
+        w = o[0, 0]
+        assert (w >= 0).all()
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+        if causal:
+            assert np.all(np.triu(w, 1) == 0)
+
+
+def pin_split_combine(orc):
+    """Partials over disjoint key ranges, combined by their lse, equal the
+    unsplit result; adding the partials (ignoring their denominators) does
+    not (smzdm digest, section 5)."""
+    B, H, N, d = 1, 2, 61, 16
+    q, k, v = synth.fwd_inputs(B, H, N, d, "bf16", seed=16)
+    qb, kb, vb = synth.to_bits(q), synth.to_bits(k), synth.to_bits(v)
+    rows = np.array([(0, h, i) for h in range(H) for i in (0, 5, 30, 60)])
+    full_o, full_lse = orc.attention_rows(qb, kb, vb, "bf16", rows, False, 0.25)
+    for bounds in ([0, 61], [0, 30, 61], [0, 1, 2, 61], [0, 20, 20, 40, 61],
+                   [0, 7, 14, 21, 28, 35, 42, 49, 56, 61]):
+        parts = [orc.attention_rows(qb, kb, vb, "bf16", rows, False, 0.25, lo, hi)
+                 for lo, hi in zip(bounds[:-1], bounds[1:])]
+        po = np.stack([p[0] for p in parts], axis=1)   # [rows, nsplit, d]
+        pl = np.stack([p[1] for p in parts], axis=1)   # [rows, nsplit]
+        for r in range(len(rows)):
+            o, lse = orc.combine(po[r], pl[r])
+            np.testing.assert_allclose(o, full_o[r], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(lse, full_lse[r], rtol=1e-13, atol=1e-13)
+        if len(parts) > 1:
+            naive = po.sum(axis=1)
+            assert np.abs(naive - full_o).max() > 1e-2
+
+
+def pin_permutation_invariance(orc):
+    """Non-causal attention does not depend on the order of the key/value
+    rows when K and V are permuted together."""
+    q, k, v = synth.fwd_inputs(1, 1, 40, 16, "fp16", seed=17)
+    qb, kb, vb = synth.to_bits(q), synth.to_bits(k), synth.to_bits(v)
+    perm = np.random.default_rng(0).permutation(40)
+    o1, l1 = orc.attention(qb, kb, vb, "fp16", False, 0.25)
+    o2, l2 = orc.attention(qb, kb[:, :, perm].copy(), vb[:, :, perm].copy(), "fp16", False, 0.25)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=1e-13, atol=1e-13)
+
+
+def _torch_reference(qb, kb, vb, dtype, causal, scale):
+    q = torch.from_numpy(widened(qb, dtype))
+    k = torch.from_numpy(widened(kb, dtype))
+    v = torch.from_numpy(widened(vb, dtype))
+    group = q.shape[1] // k.shape[1]
+    k = k.repeat_interleave(group, dim=1)
+    v = v.repeat_interleave(group, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal, scale=scale)
+    s = scale * (q @ k.transpose(-1, -2).contiguous())
+    if causal:
+        mask = torch.ones(s.shape[-2:], dtype=torch.bool).triu(1)
+        s = s.masked_fill(mask, float("-inf"))
+    return o.numpy(), torch.logsumexp(s, dim=-1).numpy()
+
+
+def pin_library_routine(orc):
+    """torch's CPU fp64 scaled_dot_product_attention and logsumexp."""
+    for dtype, causal, shape, scale in (("bf16", False, (2, 2, 33, 64), 0.125),
+                                        ("fp16", True, (1, 3, 70, 32), 1 / math.sqrt(32)),
+                                        ("bf16", True, (1, 1, 128, 128), 1 / math.sqrt(128))):
+        q, k, v = synth.fwd_inputs(*shape, dtype, seed=18)
+        qb, kb, vb = synth.to_bits(q), synth.to_bits(k), synth.to_bits(v)
+        o, lse = orc.attention(qb, kb, vb, dtype, causal, scale)
+        ro, rl = _torch_reference(qb, kb, vb, dtype, causal, scale)
+        np.testing.assert_allclose(o, ro, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse, rl, rtol=1e-12, atol=1e-12)
+
+
+def _brute(qw, kw, vw, causal, scale):
+    """Pure Python, math.fsum, softmax as exp(s) / sum exp(s) directly."""
+    Nq, d = len(qw), len(qw[0])
+    out, lses = [], []
+    for i in range(Nq):
+        keys = [j for j in range(len(kw)) if (not causal or j <= i)]
+        e = [math.exp(scale * math.fsum(qw[i][c] * kw[j][c] for c in range(d))) for j in keys]
+        z = math.fsum(e)
+        out.append([math.fsum(e[t] * vw[j][c] for t, j in enumerate(keys)) / z
+                    for c in range(len(vw[0]))])
+        lses.append(math.log(z))
+    return out, lses
+
+
+def pin_brute_force(orc):
+    for dtype, causal, N, d in (("bf16", False, 9, 5), ("fp16", True, 12, 7), ("bf16", True, 16, 8)):
+        q, k, v = synth.fwd_inputs(1, 2, N, d, dtype, seed=19)
+        qb, kb, vb = synth.to_bits(q), synth.to_bits(k), synth.to_bits(v)
+        o, lse = orc.attention(qb, kb, vb, dtype, causal, 0.4)
+        qw, kw, vw = widened(qb, dtype), widened(kb, dtype), widened(vb, dtype)
+        for h in range(2):
+            bo, bl = _brute(qw[0, h].tolist(), kw[0, h].tolist(), vw[0, h].tolist(), causal, 0.4)
+            np.testing.assert_allclose(o[0, h], np.array(bo), rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(lse[0, h], np.array(bl), rtol=1e-13, atol=1e-13)
+
+
+def pin_decode_gqa(orc):
+    """Decode = the definition with one query per (b, hq) against KV head
+    hq // (Hq/Hkv): KV heads made distinguishable by a constant V per head,
+    so O[b, hq] = that head's constant; plus the forward row definition."""
+    B, Hq, Hkv, L, d = 2, 8, 2, 19, 16
+    q, k, _ = synth.decode_inputs(B, Hq, Hkv, L, d, "bf16", seed=20)
+    vconst = np.zeros((B, Hkv, L, d), np.float32)
+    for b in range(B):
+        for g in range(Hkv):
+            vconst[b, g] = 10 * b + g + 1
+    vb = bits_of(vconst, "bf16")
+    qb, kb = synth.to_bits(q), synth.to_bits(k)
+    o, lse = orc.decode(qb, kb, vb, "bf16")
+    for b in range(B):
+        for hq in range(Hq):
+            np.testing.assert_allclose(o[b, hq], 10 * b + hq // (Hq // Hkv) + 1, rtol=1e-12)
+    # lse against the library routine with repeat_interleave'd heads
+    _, rl = _torch_reference(qb[:, :, None], kb, vb, "bf16", False, 1 / math.sqrt(d))
+    np.testing.assert_allclose(lse, rl[:, :, 0], rtol=1e-12, atol=1e-12)
+
+
+PINS = [pin_widen_all_patterns, pin_worked_examples, pin_single_key, pin_causal_row0,
+        pin_uniform_when_q_zero, pin_constant_v, pin_weights_sum_to_one, pin_split_combine,
+        pin_permutation_invariance, pin_library_routine, pin_brute_force, pin_decode_gqa]
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle_mod.get()
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
+def test_pin(orc, pin):
+    pin(orc)
+
+
+def test_rejects_bad_arguments(orc):
+    q = np.zeros((1, 2, 4, 8), np.uint16)
+    with pytest.raises(ValueError):
+        orc.attention_rows(q, q, q, "bf16", [(0, 5, 0)], False, 1.0)
+    with pytest.raises(ValueError):
+        orc.attention_rows(q, np.zeros((1, 3, 4, 8), np.uint16), np.zeros((1, 3, 4, 8), np.uint16),
+                           "bf16", [(0, 0, 0)], False, 1.0)
+
+
+def test_empty_key_range(orc):
+    q, k, v = synth.fwd_inputs(1, 1, 8, 8, "bf16", seed=21)
+    o, lse = orc.attention_rows(synth.to_bits(q), synth.to_bits(k), synth.to_bits(v), "bf16",
+                                [(0, 0, 3)], False, 1.0, 5, 5)
+    assert lse[0] == -np.inf and not o.any()
+    o2, l2 = orc.combine(np.zeros((3, 8)), np.full(3, -np.inf))
+    assert l2 == -np.inf and not o2.any()
+
+
+MUTANTS = {
+    1: "sign of the scale flipped",
+    2: "causal visibility j < i instead of j <= i",
+    3: "lse drops the running max",
+    4: "scores computed against V instead of K",
+    5: "grouped-query head map hq % Hkv",
+    6: "output not divided by the softmax denominator",
+    7: "combine adds the partial outputs",
+    8: "fp16 exponent bias 14",
+    9: "V row index off by one",
+    10: "dot product drops the last head_dim term",
+    11: "bf16 widening shifts by 15",
+    12: "combine lse drops log of the weight sum",
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=lambda m: MUTANTS[m])
+def test_pins_catch_planted_mistake(tmp_path, mutant):
+    path = oracle_mod.build(tmp_path / f"libfa_oracle_m{mutant}.so", mutant=mutant)
+    bad = oracle_mod.Oracle(path)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(bad)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {mutant}: {MUTANTS[mutant]}"
