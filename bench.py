@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path on one MI355X.
+
+One step = one fa_fwd over the forward benchmark shape (B=8, H=32, N=8192,
+d=128, fp16, non-causal: the shape of the benchmark listing on the
+dailyaiworld page "FlashAttention-3 vs Triton Kernels", section
+"Benchmarking Triton vs FlashAttention-3 Kernels") followed by one fa_decode
+over the split-KV decode shape (B=8, Hq=32, Hkv=8, L=32768, d=128, bf16,
+nsplit=16).  Inputs are seeded synthetic tensors already resident in HBM.
+
+FLOPs follow the listing's convention, 4*B*H*N^2*d (halved when causal).
+Algorithmic bytes: forward reads Q, K, V once and writes O (fp32) and lse
+once; decode reads the K and V caches once (GQA: each kv head once), q once,
+and writes O once.  Timing: W warm-up steps, then K timed steps between a
+synchronize on both sides; HIP events recorded on the launch stream between
+the two calls of every step give each call's average duration.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOPS + % MFMA peak (B8 H32 N8192 d128); decode HBM GB/s"
+PEAK_MFMA_TFLOPS = 2516.6     # MI355X dense fp16/bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+FWD = dict(B=8, H=32, N=8192, d=128, dtype="fp16", causal=False, seed=1002)
+DEC = dict(B=8, Hq=32, Hkv=8, L=32768, d=128, dtype="bf16", nsplit=16, seed=1005)
+KV_COPIES = 4                 # decode rotates among this many caches (4 GiB > 256 MB MALL)
+
+
+def fwd_flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def fwd_bytes(B, H, N, d, esize=2):
+    return 3 * B * H * N * d * esize + B * H * N * d * 4 + B * H * N * 4
+
+
+def decode_bytes(B, Hq, Hkv, L, d, esize=2):
+    return 2 * B * Hkv * L * d * esize + B * Hq * d * esize + B * Hq * d * 4
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "flashattention_attention_fa_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, digest, launches_per_unit=1):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None
+    when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(seconds_target=15.0):
+    """The fp64 oracle on a bounded sample of forward rows of the benchmark
+    shape, on this host's cores."""
+    import numpy as np
+    from flashattention_attention_fa_amd import synth
+    from oracle import oracle as oracle_mod
+
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    threads = int(os.environ["OMP_NUM_THREADS"])
+    B, H, N, d = FWD["B"], FWD["H"], FWD["N"], FWD["d"]
+    # the oracle only reads the heads the sampled rows touch: 4 heads of batch 0
+    q, k, v = synth.fwd_inputs(1, 4, N, d, FWD["dtype"], seed=FWD["seed"], device="cpu")
+    qb, kb, vb = synth.to_bits(q), synth.to_bits(k), synth.to_bits(v)
+    orc = oracle_mod.get()
+    scale = 1 / math.sqrt(d)
+    per_row = 4.0 * N * d
+    n = max(threads * 4, 32)
+    rows = synth.sample_rows(1, 4, N, n, seed=7)
+    t0 = time.perf_counter()
+    orc.attention_rows(qb, kb, vb, FWD["dtype"], rows, False, scale)
+    dt = time.perf_counter() - t0
+    n2 = int(min(1 * N * 4, max(n, n * seconds_target / max(dt, 1e-3))))
+    rows = synth.sample_rows(1, 4, N, n2, seed=8)
+    t0 = time.perf_counter()
+    orc.attention_rows(qb, kb, vb, FWD["dtype"], rows, False, scale)
+    dt = time.perf_counter() - t0
+    rate = n2 * per_row / dt
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n2} random query rows of the forward benchmark shape (each against all "
+                      f"{N} keys, d={d}, fp64), {dt:.1f} s; full problem extrapolated "
+                      f"{fwd_flops(B, H, N, d, False) / rate:.0f} s",
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["fwd", "decode"], default=None,
+                    help="time one call only (for profiling runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy, 3 times (the reference "
+                         "kernel that scales the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import flashattention_attention_fa_amd as fa
+    from flashattention_attention_fa_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.calibrate_copy:
+        n = 1 << 28                        # 2^28 fp32 = 1 GiB
+        x = torch.ones(n, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 3}))
+        return
+
+    c = FWD
+    q, k, v = synth.fwd_inputs(c["B"], c["H"], c["N"], c["d"], c["dtype"], seed=c["seed"], device=dev)
+    o = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    scale = 1 / math.sqrt(c["d"])
+
+    dcfg = DEC
+    caches = []
+    for i in range(KV_COPIES):
+        dq, dk, dv = synth.decode_inputs(dcfg["B"], dcfg["Hq"], dcfg["Hkv"], dcfg["L"], dcfg["d"],
+                                         dcfg["dtype"], seed=dcfg["seed"] + i, device=dev)
+        caches.append((dq, dk, dv))
+    do = torch.empty(caches[0][0].shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_workspace_bytes(dcfg["B"], dcfg["Hq"], dcfg["d"], dcfg["nsplit"]),
+                     dtype=torch.uint8, device=dev)
+    dlse = torch.empty(caches[0][0].shape[:2], dtype=torch.float32, device=dev)
+
+    run_fwd = args.only in (None, "fwd")
+    run_dec = args.only in (None, "decode")
+
+    def step(i):
+        if run_fwd:
+            fa.fwd(q, k, v, causal=c["causal"], scale=scale, out=o, lse=lse, stream=stream)
+        if ev is not None:
+            ev[i][1].record(stream)
+        if run_dec:
+            dq, dk, dv = caches[i % KV_COPIES]
+            fa.decode(dq, dk, dv, nsplit=dcfg["nsplit"], out=do, lse=dlse, workspace=ws, stream=stream)
+
+    ev = None
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    dec_ms = sum(b.elapsed_time(e) for _, b, e in ev) / args.steps
+    step_ms = sum(a.elapsed_time(e) for a, _, e in ev) / args.steps
+
+    flops = fwd_flops(c["B"], c["H"], c["N"], c["d"], c["causal"])
+    tflops = flops / (fwd_ms * 1e-3) / 1e12 if run_fwd else 0.0
+    dbytes = decode_bytes(dcfg["B"], dcfg["Hq"], dcfg["Hkv"], dcfg["L"], dcfg["d"])
+    gbs = dbytes / (dec_ms * 1e-3) / 1e9 if run_dec else 0.0
+    fwd_digest = source_digest("fa_fwd.hip", "fa_device.hpp")
+    dec_digest = source_digest("fa_decode.hip", "fa_device.hpp")
+    fwd_traffic = load_traffic("fa_fwd_kernel", fwd_digest)
+    dec_traffic = load_traffic("fa_decode_split_kernel", dec_digest)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c["dtype"],
+        "data": "synthetic (seeded N(0,1) tensors, inputs resident in HBM)",
+        "config": {
+            "workload": f"attention forward B{c['B']} H{c['H']} N{c['N']} d{c['d']} {c['dtype']} "
+                        f"non-causal, plus split-KV decode B{dcfg['B']} Hq{dcfg['Hq']} "
+                        f"Hkv{dcfg['Hkv']} L{dcfg['L']} d{dcfg['d']} {dcfg['dtype']} "
+                        f"nsplit{dcfg['nsplit']}",
+            "fwd": {k_: c[k_] for k_ in ("B", "H", "N", "d", "dtype", "causal")},
+            "decode": {k_: dcfg[k_] for k_ in ("B", "Hq", "Hkv", "L", "d", "dtype", "nsplit")},
+        },
+        "roofline": {
+            "kernel": "fa_fwd_kernel",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
+            "traffic": fwd_traffic,
+            "algorithmic_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": fwd_bytes(c["B"], c["H"], c["N"], c["d"]),
+            "avg_launch_ms": round(fwd_ms, 4),
+            "source_digest": fwd_digest,
+        },
+        "decode": {
+            "kernels": "fa_decode_split_kernel + fa_decode_combine_kernel",
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": dec_traffic,
+            "algorithmic_bytes_per_call": dbytes,
+            "avg_call_us": round(dec_ms * 1e3, 2),
+            "kv_cache_copies_rotated": KV_COPIES,
+            "source_digest": dec_digest,
+        },
+        "wall_s_timed": round(wall, 3),
+        "device": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+"""MI355X-native exact attention: FlashAttention forward and split-KV
+flash-decode, hand-written HIP kernels for gfx950.
+
+This module is the Python binding of libfa_amd.so (C ABI in include/fa.h).
+It only marshals arguments: it checks tensor shapes, dtypes and devices,
+allocates outputs with torch (device memory and streams are all torch is
+used for) and calls the library.  Every step of the computation runs in the
+library's kernels; if the library is missing the calls raise instead of
+falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import re
+from pathlib import Path
+
+import torch
+
+__all__ = ["fwd", "decode", "decode_workspace_bytes", "lib", "FAError", "LIB_PATH",
+           "HEADER_PATH", "status_string"]
+
+LIB_PATH = Path(__file__).resolve().parent / "libfa_amd.so"
+HEADER_PATH = Path(__file__).resolve().parent.parent / "include" / "fa.h"
+
+_DTYPE = {torch.bfloat16: 0, torch.float16: 1}
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A library call returned a non-OK status."""
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfa_amd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m flashattention_attention_fa_amd.build`")
+        L = ctypes.CDLL(str(LIB_PATH))
+        P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P, I]
+        L.fa_fwd.restype = I
+        L.fa_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, P, I]
+        L.fa_decode.restype = I
+        L.fa_decode_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, I, P, S]
+        L.fa_decode_ex.restype = I
+        L.fa_decode_workspace_bytes.argtypes = [I, I, I, I]
+        L.fa_decode_workspace_bytes.restype = S
+        L.fa_status_string.argtypes = [I]
+        L.fa_status_string.restype = ctypes.c_char_p
+        L.fa_version.argtypes = []
+        L.fa_version.restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/fa.h declares."""
+    text = re.sub(r"/\*.*?\*/", "", HEADER_PATH.read_text(), flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(fa_[a-z_]+)\s*\(",
+                      text, flags=re.M)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise FAError(f"{what}: {status_string(status)} (status {status})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
+        return_lse: bool = True, stream=None):
+    """Exact attention forward.  q, k, v: [B, H, N, d] bf16/fp16 CUDA tensors.
+    Returns (o [B, H, N, d] fp32, lse [B, H, N] fp32 or None)."""
+    _need(q.dim() == 4 and q.shape == k.shape == v.shape, "q, k, v must share a [B,H,N,d] shape")
+    _need(q.dtype in _DTYPE and q.dtype == k.dtype == v.dtype, "q, k, v must all be bf16 or fp16")
+    _need(q.is_cuda and k.device == q.device and v.device == q.device, "tensors must be on one GPU")
+    _need(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "tensors must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    _need(out.shape == q.shape and out.dtype == torch.float32 and out.is_contiguous()
+          and out.device == q.device, "out must be a contiguous fp32 [B,H,N,d] tensor")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse.shape == (B, H, N) and lse.dtype == torch.float32 and lse.is_contiguous()
+              and lse.device == q.device, "lse must be a contiguous fp32 [B,H,N] tensor")
+    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                      int(bool(causal)), float(scale), _stream(stream, q.device), _DTYPE[q.dtype])
+    _check(st, "fa_fwd")
+    return out, lse
+
+
+def decode_workspace_bytes(B: int, Hq: int, d: int, nsplit: int) -> int:
+    return int(lib().fa_decode_workspace_bytes(B, Hq, d, nsplit))
+
+
+def decode(q, kcache, vcache, *, nsplit: int, out=None, lse=None, return_lse: bool = False,
+           workspace=None, stream=None):
+    """Split-KV flash-decode.  q: [B, Hq, d]; kcache, vcache: [B, Hkv, L, d].
+    With return_lse, an lse buffer or a workspace given, the call goes through
+    fa_decode_ex (caller-owned workspace, allocated here with torch if not
+    given); otherwise through fa_decode (library-managed workspace).
+    Returns (o [B, Hq, d] fp32, lse [B, Hq] fp32 or None)."""
+    _need(q.dim() == 3 and kcache.dim() == 4 and kcache.shape == vcache.shape,
+          "q must be [B,Hq,d] and the caches [B,Hkv,L,d]")
+    B, Hq, d = q.shape
+    Bk, Hkv, L, dk = kcache.shape
+    _need(Bk == B and dk == d, "batch / head_dim mismatch between q and the caches")
+    _need(q.dtype in _DTYPE and q.dtype == kcache.dtype == vcache.dtype, "bf16 or fp16 inputs")
+    _need(q.is_cuda and kcache.device == q.device and vcache.device == q.device, "one GPU")
+    _need(q.is_contiguous() and kcache.is_contiguous() and vcache.is_contiguous(), "contiguous")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out.shape == (B, Hq, d) and out.dtype == torch.float32 and out.is_contiguous(),
+          "out must be a contiguous fp32 [B,Hq,d] tensor")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    s = _stream(stream, q.device)
+    if lse is None and workspace is None:
+        st = lib().fa_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(out), B, Hq, Hkv, L, d,
+                             int(nsplit), s, _DTYPE[q.dtype])
+        _check(st, "fa_decode")
+        return out, None
+    if workspace is None:
+        nbytes = decode_workspace_bytes(B, Hq, d, max(1, min(int(nsplit), L)))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib().fa_decode_ex(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(out), _ptr(lse), B, Hq,
+                            Hkv, L, d, int(nsplit), s, _DTYPE[q.dtype], _ptr(workspace),
+                            workspace.numel() * workspace.element_size())
+    _check(st, "fa_decode_ex")
+    return out, lse

@@ -1,0 +1,283 @@
+// fa_fwd.hip -- exact attention forward for gfx950 (MI355X).
+//
+// What it computes: softmax(scale * Q K^T [+ causal mask]) V and the per-row
+// natural log-sum-exp, tile by tile, never writing the N x N score matrix
+// (dailyaiworld page "FlashAttention-3 vs Triton Kernels", introduction).
+// The running-max / running-sum rescaling is the "online normalisation"
+// the smzdm digest (section 6) tells multi-GPU users to check first.
+//
+// Work split: one workgroup = 4 waves = 128 queries of one (batch, head);
+// each wave owns 32 queries.  Keys stream through LDS in tiles of 64, double
+// buffered: while the waves run MFMA on tile j, the next tile's K and V rows
+// are already in flight from global memory into registers, and are written
+// to the other LDS buffer afterwards (one barrier per tile).  The dailyaiworld
+// page's Hopper design gives loading and math to different warps; here every
+// wave does both, in program order, and the overlap comes from the in-flight
+// loads plus two resident workgroups per CU interleaving their MFMA and
+// softmax phases.
+//
+// Per wave and tile (32 queries x 64 keys):
+//   S^T = K Q^T   4 x 8 MFMA 32x32x16; Q lives in registers for the whole
+//                 loop (B operand), K rows come from LDS (A operand).  Each
+//                 lane then owns the scores of ONE query (its column), so the
+//                 row max / row sum are in-lane plus one exchange with the
+//                 other lane half.
+//   online softmax in the exp2 domain with c = scale*log2(e):
+//                 m' = max(m, c*max_j s_j);  alpha = 2^(m - m');
+//                 p_j = 2^(c*s_j - m');  l = alpha*l + sum p_j;  O *= alpha
+//   O^T += V^T P^T  P^T is the S^T accumulator converted to 16 bits in
+//                 place (the key order of K rows makes the accumulator layout
+//                 equal the B-operand layout), V^T is read from LDS where the
+//                 V tile was stored transposed.
+// Epilogue: O /= l, lse = (m + log2 l) * ln 2, both fp32.
+#include "fa_device.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+template <int D>
+struct FwdTile {
+    static constexpr int BM = 128;                // queries per workgroup
+    static constexpr int BN = 64;                 // keys per tile
+    static constexpr int THREADS = 256;
+    static constexpr int KLD = D + 8;             // K tile row stride (elements)
+    static constexpr int VLD = BN + 8;            // V^T tile row stride (elements)
+    static constexpr int KCH = D / 8;             // 16-byte chunks per row
+    static constexpr int K_LOADS = BN * KCH / THREADS;
+    static constexpr int V_GROUPS = (BN / 4) * KCH;   // 4 keys x 8 dims each
+    static constexpr int K_ELEMS = BN * KLD;
+    static constexpr int V_ELEMS = D * VLD;
+    static_assert(BN * KCH % THREADS == 0, "K tile must split evenly");
+    static_assert(V_GROUPS <= THREADS, "one V group per thread at most");
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, float *__restrict__ o,
+    float *__restrict__ lse, int BH, int N, int nq, float c, uint32_t qand,
+    uint32_t qxor) {
+    typedef FwdTile<D> C;
+    typedef typename T::vec8 vec8;
+    typedef typename T::scalar scalar;
+    constexpr int BM = C::BM, BN = C::BN;
+
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][C::V_ELEMS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int li = lane & 31;   // query column inside the wave's 32
+    const int lh = lane >> 5;   // lane half
+
+    // Block -> (q-tile, head).  Non-causal: consecutive logical ids walk the
+    // q-tiles of one head (K/V stay hot in that XCD's L2).  Causal: the
+    // longest q-tiles (most keys) start first.
+    const unsigned id = xcd_remap(blockIdx.x, gridDim.x);
+    int qt, bh;
+    if (CAUSAL) {
+        qt = nq - 1 - (int)(id / (unsigned)BH);
+        bh = (int)(id % (unsigned)BH);
+    } else {
+        bh = (int)(id / (unsigned)nq);
+        qt = (int)(id % (unsigned)nq);
+    }
+    const size_t head = (size_t)bh * N * D;
+    const uint16_t *qh = q + head, *kh = k + head, *vh = v + head;
+    const int q0 = qt * BM;
+    const int qw = q0 + wave * 32;   // first query of this wave
+    const int my_q = qw + li;
+
+    // Q fragments: B operand, lane (li, lh) holds row my_q, dims 16t+8lh..+8.
+    vec8 qf[D / 16];
+    {
+        const bool ok = my_q < N;
+        const uint16_t *src = qh + (size_t)(ok ? my_q : 0) * D + 8 * lh;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+            u32x4 x = ok ? *(const u32x4 *)(src + 16 * t) : zero4();
+            // scale < 0: flip the sign of q (exact) and use |scale|;
+            // scale == 0: every visible score is 0, i.e. q = 0.
+            x = (x & qand) ^ qxor;
+            qf[t] = as_vec8<vec8>(x);
+        }
+    }
+
+    const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+    const int ntiles = (kv_end + BN - 1) / BN;
+
+    u32x4 kreg[C::K_LOADS];
+    u32x4 vreg[4];
+
+    auto load_tile = [&](int kv0) {
+#pragma unroll
+        for (int r = 0; r < C::K_LOADS; ++r) {
+            const int ch = tid + C::THREADS * r;
+            const int row = ch / C::KCH, col = ch % C::KCH;
+            const int key = kv0 + row;
+            kreg[r] = key < N ? *(const u32x4 *)(kh + (size_t)key * D + col * 8) : zero4();
+        }
+        if (tid < C::V_GROUPS) {
+            const int dc = tid % C::KCH, kg = tid / C::KCH;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = kv0 + 4 * kg + r;
+                vreg[r] = key < N ? *(const u32x4 *)(vh + (size_t)key * D + dc * 8) : zero4();
+            }
+        }
+    };
+
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int r = 0; r < C::K_LOADS; ++r) {
+            const int ch = tid + C::THREADS * r;
+            const int row = ch / C::KCH, col = ch % C::KCH;
+            *(u32x4 *)&Ks[buf][row * C::KLD + col * 8] = kreg[r];
+        }
+        if (tid < C::V_GROUPS) {
+            const int dc = tid % C::KCH, kg = tid / C::KCH;
+            uint16_t *dst = &Vt[buf][(dc * 8) * C::VLD + 4 * kg];
+#define FA_VT_STORE(E)                                                        \
+    *(u32x2 *)(dst + (E) * C::VLD) =                                          \
+        u32x2{pack_col<E>(vreg[0], vreg[1]), pack_col<E>(vreg[2], vreg[3])};
+            FA_VT_STORE(0) FA_VT_STORE(1) FA_VT_STORE(2) FA_VT_STORE(3)
+            FA_VT_STORE(4) FA_VT_STORE(5) FA_VT_STORE(6) FA_VT_STORE(7)
+#undef FA_VT_STORE
+        }
+    };
+
+    floatx16 oacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    const int kp = key_perm(li);
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        const int kv0 = j * BN;
+        if (j + 1 < ntiles) load_tile(kv0 + BN);
+
+        // Causal: a wave whose queries all precede the tile has nothing to do.
+        const bool active = !CAUSAL || kv0 <= qw + 31;
+        if (active) {
+            floatx16 s[BN / 32];
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+                const uint16_t *ka = &Ks[buf][(32 * kb + kp) * C::KLD + 8 * lh];
+#pragma unroll
+                for (int t = 0; t < D / 16; ++t)
+                    s[kb] = T::mfma32(as_vec8<vec8>(*(const u32x4 *)(ka + 16 * t)), qf[t], s[kb]);
+            }
+
+            // Mask keys past the end and, on diagonal tiles, keys after the query.
+            const bool need_mask = (kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > qw);
+            if (need_mask) {
+                const int lim = CAUSAL ? min(N - 1, my_q) : N - 1;
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kv0 + 32 * kb + 16 * (r >> 3) + 8 * lh + (r & 7);
+                        if (key > lim) s[kb][r] = -INFINITY;
+                    }
+            }
+
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = fmaxf(mx, other_half(mx));
+            const float m_new = fmaxf(m_run, mx * c);
+            const float mb = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mb);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mb));
+                    s[kb][r] = p;
+                    l_run += p;
+                }
+
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    vec8 pb;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pb[e] = (scalar)s[kb][8 * u + e];
+                    const uint16_t *va = &Vt[buf][li * C::VLD + 32 * kb + 16 * u + 8 * lh];
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+                        oacc[db] = T::mfma32(
+                            as_vec8<vec8>(*(const u32x4 *)(va + 32 * db * C::VLD)), pb, oacc[db]);
+                }
+        }
+
+        if (j + 1 < ntiles) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue.  O^T accumulator: lane (li, lh), register r of block db holds
+    // dim 32*db + 8*(r/4) + 4*lh + r%4 of query my_q.
+    const float l_tot = l_run + other_half(l_run);
+    if (my_q < N) {
+        const float inv = 1.f / l_tot;
+        float *orow = o + head + (size_t)my_q * D + 4 * lh;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                *(floatx4 *)(orow + 32 * db + 8 * a) =
+                    floatx4{oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv,
+                            oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv};
+        if (lse != nullptr && lh == 0)
+            lse[(size_t)bh * N + my_q] = (m_run + log2f(l_tot)) * kLn2;
+    }
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch(const FwdArgs &a, hipStream_t stream) {
+    typedef FwdTile<D> C;
+    const int nq = (a.N + C::BM - 1) / C::BM;
+    const long long blocks = (long long)nq * a.BH;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const bool zero = a.scale == 0.f;
+    const float c = zero ? kLog2e : fabsf(a.scale) * kLog2e;
+    const uint32_t qand = zero ? 0u : 0xffffffffu;
+    const uint32_t qxor = a.scale < 0.f ? 0x80008000u : 0u;
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(C::THREADS),
+                       0, stream, (const uint16_t *)a.q, (const uint16_t *)a.k,
+                       (const uint16_t *)a.v, a.o, a.lse, a.BH, a.N, nq, c, qand, qxor);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_dtype(const FwdArgs &a, hipStream_t s) {
+    if (a.d == 128) return a.causal ? launch<T, 128, true>(a, s) : launch<T, 128, false>(a, s);
+    if (a.d == 64) return a.causal ? launch<T, 64, true>(a, s) : launch<T, 64, false>(a, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream) {
+    return a.dtype == 1 ? launch_dtype<FP16>(a, stream) : launch_dtype<BF16>(a, stream);
+}
+
+}  // namespace fa

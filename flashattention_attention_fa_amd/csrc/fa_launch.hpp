@@ -1,0 +1,35 @@
+// fa_launch.hpp -- host-side launchers implemented in the .hip files and
+// called by the C ABI layer (fa_api.cpp) after it has validated arguments.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+    const void *q, *k, *v;  // [BH, N, d] 16-bit
+    float *o;               // [BH, N, d]
+    float *lse;             // [BH, N] or nullptr
+    int BH, N, d;
+    bool causal;
+    float scale;
+    int dtype;              // 0 bf16, 1 fp16
+};
+
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
+
+struct DecodeArgs {
+    const void *q;          // [B, Hq, d] 16-bit
+    const void *k, *v;      // [B, Hkv, L, d] 16-bit
+    float *o;               // [B, Hq, d]
+    float *lse;             // [B, Hq] or nullptr
+    float *ws_o;            // [B, Hq, nsplit, d]
+    float *ws_lse;          // [B, Hq, nsplit]
+    int B, Hq, Hkv, L, d, nsplit, chunk;
+    int dtype;
+};
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,115 @@
+/*
+ * fa.h -- C ABI of libfa_amd.so: exact attention forward (FlashAttention
+ * tiling, online softmax, log-sum-exp) and split-KV flash-decode for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Plain pointers and sizes only.  Every tensor pointer is a DEVICE pointer
+ * owned by the caller; the library keeps none of them after a call returns
+ * and frees nothing it did not allocate.  All calls enqueue work on `stream`
+ * (0 = the null stream) and return without synchronising; a fault inside a
+ * kernel surfaces at the caller's next synchronisation.  Argument checks run
+ * before any HIP call, so a rejected call has enqueued nothing.
+ *
+ * Layouts are contiguous with head_dim fastest, the (batch, heads, seq_len,
+ * head_dim) convention of the benchmark listing on the dailyaiworld page
+ * "FlashAttention-3 vs Triton Kernels: Warp-Specialization on GPUs",
+ * section "Benchmarking Triton vs FlashAttention-3 Kernels".
+ */
+#ifndef FA_AMD_FA_H
+#define FA_AMD_FA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    FA_ERR_SHAPE = 2,       /* a size is negative, inconsistent or too large  */
+    FA_ERR_UNSUPPORTED = 3, /* head_dim not in {64, 128}, or unknown dtype    */
+    FA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned        */
+    FA_ERR_WORKSPACE = 5,   /* caller workspace missing or too small          */
+    FA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed     */
+    FA_ERR_INTERNAL = 7,    /* unexpected internal error                      */
+    FA_ERR_VALUE = 8        /* a non-finite scale                             */
+} fa_status_t;
+
+/* Storage type of q, k, v and the caches.  Arithmetic is bf16/fp16 products
+ * with fp32 accumulation; outputs are always fp32. */
+typedef enum { FA_BF16 = 0, FA_FP16 = 1 } fa_dtype_t;
+
+/*
+ * fa_fwd -- exact softmax attention, computed tile by tile without storing
+ * the N x N score matrix (dailyaiworld page, introduction: FlashAttention's
+ * IO-aware tiling).  For every b < B, h < H, i < N:
+ *     s_ij  = scale * <q[b,h,i,:], k[b,h,j,:]>     over visible keys j
+ *     o[b,h,i,:] = sum_j softmax_j(s_i.) * v[b,h,j,:]
+ *     lse[b,h,i] = log(sum_j exp(s_ij))            (natural log)
+ * Key j is visible to query i iff causal == 0 or j <= i.
+ *
+ *   q, k, v : [B, H, N, d] 16-bit (dtype), device, 16-byte aligned
+ *   o       : [B, H, N, d] fp32, device, 16-byte aligned (written)
+ *   lse     : [B, H, N]    fp32, device, 4-byte aligned, or NULL to skip
+ *   d       : 64 or 128
+ *   scale   : finite; 1/sqrt(d) reproduces the usual default
+ * B == 0, H == 0 or N == 0 is a no-op returning FA_OK.
+ */
+fa_status_t fa_fwd(const void *q, const void *k, const void *v, float *o,
+                   float *lse, int B, int H, int N, int d, int causal,
+                   float scale, hipStream_t stream, fa_dtype_t dtype);
+
+/*
+ * fa_decode -- attention of one new query token per sequence against a
+ * key/value cache, split along the cache length into nsplit shards whose
+ * partial results (O_s, lse_s) are combined by log-sum-exp reweighting
+ * (post.smzdm.com digest on Triton warp specialisation, section 5: shard
+ * outputs cannot simply be added; each carries its lse and the combine
+ * re-normalises with it):
+ *     lse = log sum_s exp(lse_s),   o = sum_s exp(lse_s - lse) * O_s
+ * Grouped-query attention: query head hq reads key/value head
+ * hq / (Hq / Hkv).  Every cached key is visible; scale is 1/sqrt(d).
+ *
+ *   q              : [B, Hq, d]       16-bit, device, 16-byte aligned
+ *   kcache, vcache : [B, Hkv, L, d]   16-bit, device, 16-byte aligned
+ *   o              : [B, Hq, d]       fp32, device, 16-byte aligned (written)
+ *   Hq % Hkv == 0; L >= 1; nsplit >= 1 (clamped to L; shard s covers keys
+ *   [s*C, min(L, (s+1)*C)) with C = ceil(L / nsplit)).
+ * Partial results live in a per-device workspace that the library allocates
+ * on first use and grows when a larger call needs it (guarded by a mutex;
+ * calls on different streams of one device share it, so such calls must not
+ * overlap in time).  B == 0 or Hq == 0 is a no-op returning FA_OK.
+ */
+fa_status_t fa_decode(const void *q, const void *kcache, const void *vcache,
+                      float *o, int B, int Hq, int Hkv, int L, int d,
+                      int nsplit, hipStream_t stream, fa_dtype_t dtype);
+
+/* Bytes of workspace fa_decode_ex needs for these sizes (0 on bad sizes). */
+size_t fa_decode_workspace_bytes(int B, int Hq, int d, int nsplit);
+
+/*
+ * fa_decode_ex -- fa_decode with the final lse (optional) and a
+ * caller-owned device workspace of at least fa_decode_workspace_bytes()
+ * bytes, 256-byte aligned (FA_ERR_WORKSPACE otherwise).  Calls sharing one
+ * workspace must not overlap in time.
+ *   lse : [B, Hq] fp32, device, or NULL
+ */
+fa_status_t fa_decode_ex(const void *q, const void *kcache,
+                         const void *vcache, float *o, float *lse, int B,
+                         int Hq, int Hkv, int L, int d, int nsplit,
+                         hipStream_t stream, fa_dtype_t dtype,
+                         void *workspace, size_t workspace_bytes);
+
+/* Static English description of a status code. */
+const char *fa_status_string(fa_status_t status);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_AMD_FA_H */

@@ -1,0 +1,114 @@
+"""The C ABI on the CPU: libfa_amd.so loads, exports every function
+include/fa.h declares, and rejects bad arguments with the documented status
+before touching the GPU (no kernel is launched by these tests)."""
+import ctypes
+
+import pytest
+
+import flashattention_attention_fa_amd as fa
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, INTERNAL, VALUE = range(9)
+A = 0x10000          # a 16-byte aligned fake device address (never dereferenced)
+MIS = 0x10008        # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def L():
+    return fa.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = fa.declared_functions()
+    assert set(names) >= {"fa_fwd", "fa_decode", "fa_decode_ex", "fa_decode_workspace_bytes",
+                          "fa_status_string", "fa_version"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(9):
+        assert fa.status_string(s)
+    assert fa.status_string(99) == "unknown status"
+    assert L.fa_version() >= 100
+
+
+def fwd(L, q=A, k=A, v=A, o=A, lse=None, B=1, H=1, N=16, d=64, causal=0, scale=0.125, dtype=0):
+    return L.fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, None, dtype)
+
+
+def test_fwd_validation(L):
+    assert fwd(L, q=None) == NULL
+    assert fwd(L, o=None) == NULL
+    assert fwd(L, B=-1) == SHAPE
+    assert fwd(L, N=-5) == SHAPE
+    assert fwd(L, d=96) == UNSUP
+    assert fwd(L, d=256) == UNSUP
+    assert fwd(L, dtype=7) == UNSUP
+    assert fwd(L, k=MIS) == ALIGN
+    assert fwd(L, o=MIS) == ALIGN
+    assert fwd(L, lse=A + 2) == ALIGN
+    assert fwd(L, scale=float("nan")) == VALUE
+    assert fwd(L, scale=float("inf")) == VALUE
+    assert fwd(L, N=(1 << 30) + 1) == SHAPE
+    assert fwd(L, B=65536, H=65536) == SHAPE
+
+
+def test_fwd_empty_is_noop(L):
+    # no pointer is needed when there is nothing to compute
+    assert fwd(L, q=None, k=None, v=None, o=None, B=0) == OK
+    assert fwd(L, q=None, k=None, v=None, o=None, H=0) == OK
+    assert fwd(L, q=None, k=None, v=None, o=None, N=0) == OK
+
+
+def dec(L, q=A, k=A, v=A, o=A, B=1, Hq=4, Hkv=2, Lk=100, d=128, nsplit=4, dtype=0):
+    return L.fa_decode(q, k, v, o, B, Hq, Hkv, Lk, d, nsplit, None, dtype)
+
+
+def dec_ex(L, ws=A, ws_bytes=1 << 20, lse=None, **kw):
+    a = dict(q=A, k=A, v=A, o=A, B=1, Hq=4, Hkv=2, Lk=100, d=128, nsplit=4, dtype=0)
+    a.update(kw)
+    return L.fa_decode_ex(a["q"], a["k"], a["v"], a["o"], lse, a["B"], a["Hq"], a["Hkv"],
+                          a["Lk"], a["d"], a["nsplit"], None, a["dtype"], ws, ws_bytes)
+
+
+def test_decode_validation(L):
+    assert dec(L, q=None) == NULL
+    assert dec(L, v=None) == NULL
+    assert dec(L, Hq=6, Hkv=4) == SHAPE
+    assert dec(L, Hkv=0) == SHAPE
+    assert dec(L, Lk=0) == SHAPE
+    assert dec(L, nsplit=0) == SHAPE
+    assert dec(L, d=80) == UNSUP
+    assert dec(L, dtype=3) == UNSUP
+    assert dec(L, k=MIS) == ALIGN
+    assert dec(L, B=70000) == SHAPE
+    assert dec(L, q=None, B=0) == OK
+    assert dec(L, q=None, Hq=0) == OK
+
+
+def test_decode_ex_workspace(L):
+    need = L.fa_decode_workspace_bytes(1, 4, 128, 4)
+    # ws_o = 1*4*4*128*4 = 8192 bytes, ws_lse = 64 -> 256: 8448 bytes
+    assert need == 8192 + 256
+    assert L.fa_decode_workspace_bytes(1, 4, 100, 4) == 0
+    assert L.fa_decode_workspace_bytes(1, 4, 128, 0) == 0
+    assert dec_ex(L, ws=None) == WS
+    assert dec_ex(L, ws_bytes=need - 1) == WS
+    assert dec_ex(L, ws=A + 16) == WS           # not 256-byte aligned
+    assert dec_ex(L, lse=A + 1) == ALIGN
+    # nsplit larger than L is clamped to L before sizing the workspace
+    assert L.fa_decode_workspace_bytes(1, 4, 128, 100) < L.fa_decode_workspace_bytes(1, 4, 128, 200)
+    assert dec_ex(L, Lk=3, nsplit=50, ws_bytes=L.fa_decode_workspace_bytes(1, 4, 128, 3) - 1) == WS
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q.float())
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q[:, :1])
+    with pytest.raises(ValueError):      # CPU tensors are rejected before any call
+        fa.fwd(q, q, q)
+    with pytest.raises(ValueError):
+        fa.decode(q[:, :, 0], q, q.half(), nsplit=2)

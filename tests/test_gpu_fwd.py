@@ -1,0 +1,145 @@
+"""fa_fwd through the C ABI on an MI355X, against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import flashattention_attention_fa_amd as fa
+from flashattention_attention_fa_amd import synth
+from oracle import oracle as oracle_mod
+from parity import assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle_mod.get()
+
+
+def run_full(orc, B, H, N, d, dtype, causal, seed, scale=None, **kw):
+    print(f"case fwd B{B} H{H} N{N} d{d} {dtype} causal={causal} seed={seed}", flush=True)
+    q, k, v = synth.fwd_inputs(B, H, N, d, dtype, seed=seed, device=DEV, **kw)
+    scale = 1 / math.sqrt(d) if scale is None else scale
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = orc.attention(synth.to_bits(q), synth.to_bits(k), synth.to_bits(v), dtype, causal, scale)
+    return assert_close(o.cpu().numpy(), ro, lse.cpu().numpy(), rl,
+                        f"fwd B{B} H{H} N{N} d{d} {dtype} causal={causal}")
+
+
+def run_rows(orc, cfg, rows):
+    c = dict(cfg)
+    print(f"case fwd {c}", flush=True)
+    q, k, v = synth.fwd_inputs(c["B"], c["H"], c["N"], c["d"], c["dtype"], seed=c["seed"],
+                               device=DEV, krow_scale=c.get("krow_scale"))
+    scale = 1 / math.sqrt(c["d"])
+    o, lse = fa.fwd(q, k, v, causal=c["causal"], scale=scale)
+    torch.cuda.synchronize()
+    r = torch.as_tensor(rows)
+    og = o[r[:, 0], r[:, 1], r[:, 2]].cpu().numpy()
+    lg = lse[r[:, 0], r[:, 1], r[:, 2]].cpu().numpy()
+    del o, lse
+    qb, kb, vb = synth.to_bits(q), synth.to_bits(k), synth.to_bits(v)
+    del q, k, v
+    torch.cuda.empty_cache()
+    ro, rl = orc.attention_rows(qb, kb, vb, c["dtype"], rows, c["causal"], scale)
+    return assert_close(og, ro, lg, rl, f"fwd sampled {len(rows)} rows")
+
+
+# -- the workloads --------------------------------------------------------------
+
+def test_tiny_config(orc):
+    c = synth.CONFIGS["tiny"]
+    run_full(orc, c["B"], c["H"], c["N"], c["d"], c["dtype"], False, c["seed"])
+    run_full(orc, c["B"], c["H"], c["N"], c["d"], c["dtype"], True, c["seed"])
+
+
+def test_bench_shape_sampled(orc):
+    c = synth.CONFIGS["fwd_b8h32n8k"]
+    rows = synth.sample_rows(c["B"], c["H"], c["N"], 256, seed=c["seed"])
+    run_rows(orc, c, rows)
+
+
+def test_causal_kscaled_sampled(orc):
+    c = synth.CONFIGS["causal_b4h32n16k_kscaled"]
+    rows = synth.boundary_rows(c["B"], c["H"], c["N"], seed=c["seed"], n_random=96)
+    run_rows(orc, c, rows)
+
+
+def test_long_causal_sampled(orc):
+    c = synth.CONFIGS["causal_b1h32n128k"]
+    rows = synth.boundary_rows(c["B"], c["H"], c["N"], seed=c["seed"], n_random=64)
+    run_rows(orc, c, rows)
+
+
+# -- several tiles with ragged tails, both dtypes and head dims ---------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_multi_tile(orc, dtype, causal, d):
+    run_full(orc, 2, 3, 333, d, dtype, causal, seed=40 + d)
+
+
+@pytest.mark.parametrize("N", [1, 2, 31, 63, 64, 65, 127, 128, 129, 191, 257])
+@pytest.mark.parametrize("causal", [False, True])
+def test_lengths(orc, N, causal):
+    run_full(orc, 1, 2, N, 128, "bf16", causal, seed=N)
+
+
+def test_single_key_returns_v(orc):
+    q, k, v = synth.fwd_inputs(2, 4, 1, 128, "bf16", seed=3, device=DEV)
+    o, lse = fa.fwd(q, k, v, scale=0.1)
+    torch.cuda.synchronize()
+    # P is rounded to 16 bits while l sums the fp32 weights: O = V within 1 ulp-ish
+    np.testing.assert_allclose(o[:, :, 0].cpu().numpy(), v[:, :, 0].float().cpu().numpy(),
+                               rtol=1e-6, atol=1e-6)
+    ref = 0.1 * (q.double() * k.double()).sum(-1)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref.cpu().numpy(), atol=1e-3)
+
+
+def test_causal_row0_and_uniform(orc):
+    N = 300
+    _, k, v = synth.fwd_inputs(1, 2, N, 128, "fp16", seed=5, device=DEV)
+    q = torch.zeros_like(k)
+    o, lse = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    vf = v.double()
+    mean = torch.cumsum(vf, dim=2) / torch.arange(1, N + 1, device=DEV, dtype=torch.float64)[:, None]
+    np.testing.assert_allclose(o.cpu().numpy(), mean.cpu().numpy(), atol=2e-3, rtol=0)
+    np.testing.assert_allclose(lse.cpu().numpy()[0, 0], np.log(np.arange(1, N + 1)), atol=1e-4)
+    np.testing.assert_allclose(o[:, :, 0].cpu().numpy(), v[:, :, 0].float().cpu().numpy(),
+                               rtol=1e-6, atol=1e-6)
+
+
+def test_constant_v(orc):
+    q, k, _ = synth.fwd_inputs(1, 2, 200, 64, "bf16", seed=6, device=DEV)
+    v = torch.full_like(q, 1.5)
+    for causal in (False, True):
+        o, _ = fa.fwd(q, k, v, causal=causal)
+        torch.cuda.synchronize()
+        assert (o - 1.5).abs().max().item() < 1e-2
+
+
+def test_scale_sign_and_zero(orc):
+    for scale in (-0.2, 0.0, 0.5):
+        run_full(orc, 1, 2, 150, 128, "bf16", True, seed=8, scale=scale)
+
+
+def test_lse_optional_and_deterministic(orc):
+    q, k, v = synth.fwd_inputs(2, 2, 500, 128, "fp16", seed=9, device=DEV)
+    o1, l1 = fa.fwd(q, k, v, causal=True)
+    o2, l2 = fa.fwd(q, k, v, causal=True, return_lse=False)
+    o3, l3 = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert l2 is None
+    assert torch.equal(o1, o2) and torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_empty_batch_is_noop():
+    q = torch.empty(0, 2, 16, 64, dtype=torch.bfloat16, device=DEV)
+    o, lse = fa.fwd(q, q, q)
+    assert o.numel() == 0 and lse.numel() == 0
