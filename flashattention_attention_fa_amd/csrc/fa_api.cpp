@@ -15,7 +15,8 @@
 
 namespace {
 
-constexpr int kMaxSeq = 1 << 30;
+// Per-head byte offsets are 32-bit (buffer addressing): seq_len * 128 * 2 < 2^32.
+constexpr int kMaxSeq = 1 << 23;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

@@ -20,15 +20,14 @@
 // the current block is computed.
 //
 // MFMA 16x16x32 (16 columns = up to 16 query heads of one group):
-//   S^T (16 keys x 16 heads) = K (16 x 32 dims) Q^T;  K rows are fed in the
-//   order that makes two S^T blocks together equal the B-operand layout of
-//   O^T (16 dims x 16 heads) += V^T (16 dims x 32 keys) P^T (32 keys x 16).
+//   S^T (16 keys x 16 heads) = K (16 x 32 dims) Q^T, K straight from global
+//   memory into A-operand registers; two S^T blocks (32 keys) form the P^T
+//   operand of O^T (16 dims x 16 heads) += V^T (16 dims x 32 keys) P^T, with
+//   V^T read from a row-major LDS copy of the V rows by transposing reads.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // 16x16x32 MFMA: A lane (i + 16g) holds row i, contraction 8g..8g+7; B lane
 // (j + 16g) holds column j, contraction 8g..8g+7; C lane (j + 16g) register
@@ -52,19 +51,19 @@ template <int D>
 struct DecTile {
     static constexpr int THREADS = 256;
     static constexpr int WAVES = 4;
-    static constexpr int BK = 32;                 // keys per wave step
-    static constexpr int COLS = 16;               // query heads per workgroup
-    static constexpr int VLD = BK + 8;            // V^T row stride (elements)
-    static constexpr int KCH = D / 8;             // 16-byte chunks per row
-    static constexpr int KPL = BK * KCH / 64;     // V rows loaded per lane
-    static constexpr int V_ELEMS = D * VLD;       // per wave
-    static_assert(KPL == 4 || KPL == 8, "V row grouping");
+    static constexpr int BK = 32;                  // keys per wave step
+    static constexpr int COLS = 16;                // query heads per workgroup
+    static constexpr int LD = D + 8;               // V tile row stride (elements)
+    static constexpr int KCH = D / 8;              // 16-byte chunks per row
+    static constexpr int VROWS = 64 / KCH;         // V rows covered by one wave load
+    static constexpr int VLOADS = BK / VROWS;      // V loads per lane per step
+    static constexpr int V_ELEMS = BK * LD;        // per wave
 };
 
 template <int D>
 struct DecBuf {
-    u32x4 kf[2][D / 32];           // K A-operands, 2 S^T blocks x D/32 steps
-    u32x4 vr[DecTile<D>::KPL];     // V rows for the LDS transpose
+    u32x4 kf[2][D / 32];               // K A-operands, 2 S^T blocks x D/32 steps
+    u32x4 vr[DecTile<D>::VLOADS];      // V rows, staged to LDS
 };
 
 template <typename T, int D>
@@ -76,9 +75,10 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
     typedef DecTile<D> C;
     typedef typename T::vec8 vec8;
     typedef typename T::scalar scalar;
+    constexpr int LD = C::LD;
 
-    // V^T staging, one slab per wave; reused for the final merge.
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[C::WAVES][C::V_ELEMS];
+    // V tile staging, one slab per wave; reused for the final merge.
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[C::WAVES][C::V_ELEMS];
     __shared__ float sm_m[C::WAVES][C::COLS], sm_l[C::WAVES][C::COLS];
 
     const int tid = threadIdx.x;
@@ -99,7 +99,9 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
     const int nblk = k_hi > k_lo ? (k_hi - k_lo + C::BK - 1) / C::BK : 0;
 
     const size_t kvhead = ((size_t)b * Hkv + g) * (size_t)L * D;
-    const uint16_t *kh = k + kvhead, *vh = v + kvhead;
+    const uint32_t head_bytes = (uint32_t)L * D * 2;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kvhead, head_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kvhead, head_bytes);
 
     // Q^T fragments: B operand, lane (lj, lg) holds head hq0+lj, dims 32t+8lg..+8.
     vec8 qf[D / 32];
@@ -111,39 +113,39 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
             qf[t] = as_vec8<vec8>(ok ? *(const u32x4 *)(src + 32 * t) : zero4());
     }
 
-    // S^T block beta, A row i holds key 8*(i/4) + 4*beta + i%4 of the 32-key
-    // block, so lane group lg ends up with keys 8lg..8lg+7 in the order the
-    // P^T operand needs (registers 0..3 of block 0, then of block 1).
-    const int krow0 = 8 * (lj >> 2) + (lj & 3);
-    // V transpose: lane (dc, vg) loads rows vg*KPL .. +KPL of dim chunk dc.
-    const int dc = lane % C::KCH, vg = lane / C::KCH;
+    // V staging: lane (dc, vrow) loads chunk dc of rows vrow + VROWS*r.
+    const int dc = lane % C::KCH, vrow = lane / C::KCH;
 
+    // Keys past L read as zero (buffer range check); keys past the shard end
+    // are masked out of the softmax below.
     auto load = [&](DecBuf<D> &bf, int n) {
         const int key0 = k_lo + C::BK * n;
 #pragma unroll
-        for (int beta = 0; beta < 2; ++beta) {
-            const int key = key0 + krow0 + 4 * beta;
-            const bool ok = key < k_hi;
-            const uint16_t *src = kh + (size_t)(ok ? key : 0) * D + 8 * lg;
+        for (int beta = 0; beta < 2; ++beta)
 #pragma unroll
             for (int t = 0; t < D / 32; ++t)
-                bf.kf[beta][t] = ok ? *(const u32x4 *)(src + 32 * t) : zero4();
-        }
+                bf.kf[beta][t] = buffer_load16(
+                    kr, (uint32_t)((key0 + 16 * beta + lj) * D + 32 * t + 8 * lg) * 2u);
 #pragma unroll
-        for (int r = 0; r < C::KPL; ++r) {
-            const int key = key0 + vg * C::KPL + r;
-            bf.vr[r] = key < k_hi ? *(const u32x4 *)(vh + (size_t)key * D + 8 * dc) : zero4();
-        }
+        for (int r = 0; r < C::VLOADS; ++r)
+            bf.vr[r] = buffer_load16(vr, (uint32_t)((key0 + vrow + C::VROWS * r) * D + 8 * dc) * 2u);
     };
 
     floatx4 oacc[D / 16];
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
-    uint16_t *vt = Vt[wave];
+    uint16_t *vt = Vs[wave];
+    // ds_read_b64_tr_b16 addressing: lane j of group lg points at row
+    // 4*lg + j/4, column 4*(j%4) (plus the 16-dim block offset).
+    const uint16_t *va = vt + (4 * lg + (lj >> 2)) * LD + 4 * (lj & 3);
 
     auto compute = [&](const DecBuf<D> &bf, int n) {
         const int key0 = k_lo + C::BK * n;
+#pragma unroll
+        for (int r = 0; r < C::VLOADS; ++r)
+            *(u32x4 *)(vt + (vrow + C::VROWS * r) * LD + 8 * dc) = bf.vr[r];
+        // S^T block beta: lane (lj, lg), register r holds key key0 + 16beta + 4lg + r.
         floatx4 sc[2];
 #pragma unroll
         for (int beta = 0; beta < 2; ++beta) {
@@ -152,28 +154,12 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
             for (int t = 0; t < D / 32; ++t)
                 sc[beta] = T::mfma16(as_vec8<vec8>(bf.kf[beta][t]), qf[t], sc[beta]);
         }
-        // Stage V^T for this block: dims 8dc..8dc+7, keys vg*KPL..+KPL.
-        {
-            uint16_t *dst = vt + (8 * dc) * C::VLD + vg * C::KPL;
-#define FA_DEC_VT(E)                                                             \
-    if constexpr (C::KPL == 8)                                                   \
-        *(u32x4 *)(dst + (E) * C::VLD) = u32x4{                                  \
-            pack_col<E>(bf.vr[0], bf.vr[1]), pack_col<E>(bf.vr[2], bf.vr[3]),    \
-            pack_col<E>(bf.vr[4], bf.vr[5]), pack_col<E>(bf.vr[6], bf.vr[7])};   \
-    else                                                                         \
-        *(u32x2 *)(dst + (E) * C::VLD) =                                         \
-            u32x2{pack_col<E>(bf.vr[0], bf.vr[1]), pack_col<E>(bf.vr[2], bf.vr[3])};
-            FA_DEC_VT(0) FA_DEC_VT(1) FA_DEC_VT(2) FA_DEC_VT(3)
-            FA_DEC_VT(4) FA_DEC_VT(5) FA_DEC_VT(6) FA_DEC_VT(7)
-#undef FA_DEC_VT
-        }
-        // key of (block beta, register r) in lane group lg: 8lg + 4beta + r
         if (key0 + C::BK > k_hi) {
 #pragma unroll
             for (int beta = 0; beta < 2; ++beta)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (key0 + 8 * lg + 4 * beta + r >= k_hi) sc[beta][r] = -INFINITY;
+                    if (key0 + 16 * beta + 4 * lg + r >= k_hi) sc[beta][r] = -INFINITY;
         }
         float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                          fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
@@ -186,6 +172,8 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
+        // P^T operand: element e holds key 4lg + e (block 0) for e < 4 and
+        // key 16 + 4lg + e - 4 (block 1) for e >= 4.
         vec8 pb;
 #pragma unroll
         for (int beta = 0; beta < 2; ++beta)
@@ -195,15 +183,16 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
                 l_run += p;
                 pb[4 * beta + r] = (scalar)p;
             }
-        // The V^T slab is private to this wave: order its LDS writes before
-        // the reads below (LDS operations of one wave complete in order).
+        // The V slab is private to this wave: order its LDS writes before the
+        // reads below (LDS operations of one wave complete in order).
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const uint16_t *va = vt + lj * C::VLD + 8 * lg;
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db)
-            oacc[db] = T::mfma16(as_vec8<vec8>(*(const u32x4 *)(va + 16 * db * C::VLD)), pb, oacc[db]);
+        for (int db = 0; db < D / 16; ++db) {
+            const vec8 vtp = join8<vec8>(lds_read_tr4(va + 16 * db), lds_read_tr4(va + 16 * LD + 16 * db));
+            oacc[db] = T::mfma16(vtp, pb, oacc[db]);
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -240,9 +229,11 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
     for (int w = 0; w < C::WAVES; ++w)
         Lsum += sm_l[w][lj] * __builtin_amdgcn_exp2f(sm_m[w][lj] - Mb);
     const float f = Lsum > 0.f ? __builtin_amdgcn_exp2f(m_run - Mb) / Lsum : 0.f;
-    // Scaled wave outputs go to LDS as part[w][col][d] (reusing the V^T slabs).
-    float *part = reinterpret_cast<float *>(&Vt[0][0]);
-    static_assert(C::WAVES * C::COLS * D * 4 <= (int)sizeof(Vt), "merge buffer");
+    // Scaled wave outputs go to LDS as part[w][col][d] (reusing the V slabs).
+    // O^T accumulator: lane (lj, lg), register r of block db holds dim
+    // 16db + 4lg + r of head hq0 + lj.
+    float *part = reinterpret_cast<float *>(&Vs[0][0]);
+    static_assert(C::WAVES * C::COLS * D * 4 <= (int)sizeof(Vs), "merge buffer");
     __syncthreads();
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
@@ -260,31 +251,64 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
             Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
-// Combine: one workgroup per (batch, query head), one thread per dim.
+__device__ __forceinline__ float block_max128(float x, float *red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    x = fmaxf(red[0], red[1]);
+    __syncthreads();
+    return x;
+}
+
+__device__ __forceinline__ float block_sum128(float x, float *red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    x = red[0] + red[1];
+    __syncthreads();
+    return x;
+}
+
+// Combine: one 128-thread workgroup per (batch, query head).  The shard
+// weights exp(lse_s - lse) are computed once per shard and shared via LDS;
+// each thread then sums one output dim over the shards.
 __global__ __launch_bounds__(128) void fa_decode_combine_kernel(
     const float *__restrict__ ws_o, const float *__restrict__ ws_lse,
     float *__restrict__ o, float *__restrict__ lse, int D, int nsplit) {
+    constexpr int kChunk = 256;
+    __shared__ float w[kChunk];
+    __shared__ float red[2];
+    const int tid = threadIdx.x;
     const size_t row = blockIdx.x;
     const float *pl = ws_lse + row * nsplit;
     const float *po = ws_o + row * (size_t)nsplit * D;
+
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pl[s]);
-    float total = -INFINITY;
-    if (M != -INFINITY) {
-        float wsum = 0.f;
-        for (int s = 0; s < nsplit; ++s) wsum += expf(pl[s] - M);
-        total = M + logf(wsum);
-    }
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float acc = 0.f;
-        if (total != -INFINITY)
-            for (int s = 0; s < nsplit; ++s) {
-                const float w = expf(pl[s] - total);
-                if (w > 0.f) acc += w * po[(size_t)s * D + d];
+    for (int s = tid; s < nsplit; s += 128) M = fmaxf(M, pl[s]);
+    M = block_max128(M, red);
+    float wsum = 0.f;
+    if (M != -INFINITY)
+        for (int s = tid; s < nsplit; s += 128) wsum += expf(pl[s] - M);
+    wsum = block_sum128(wsum, red);
+    const float total = M == -INFINITY ? -INFINITY : M + logf(wsum);
+
+    float acc = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += kChunk) {
+        const int n = min(kChunk, nsplit - s0);
+        for (int s = tid; s < n; s += 128)
+            w[s] = total == -INFINITY ? 0.f : expf(pl[s0 + s] - total);
+        __syncthreads();
+        if (tid < D)
+            for (int s = 0; s < n; ++s) {
+                const float ww = w[s];
+                if (ww > 0.f) acc += ww * po[(size_t)(s0 + s) * D + tid];
             }
-        o[row * D + d] = acc;
+        __syncthreads();
     }
-    if (lse != nullptr && threadIdx.x == 0) lse[row] = total;
+    if (tid < D) o[row * D + tid] = acc;
+    if (lse != nullptr && tid == 0) lse[row] = total;
 }
 
 template <typename T, int D>

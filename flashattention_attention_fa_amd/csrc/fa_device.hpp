@@ -14,6 +14,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -48,6 +50,34 @@ __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 // Value held by lane (l ^ 32): the other half of the wave.
 __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
 
+// Raw buffer resource over [base, base + bytes): loads beyond `bytes` return
+// zero in hardware, which gives free bounds handling for ragged tiles.
+// 0x00020000 is the gfx9-family resource word 3 for untyped raw access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane
+// j supplies the address of 4 consecutive 16-bit elements M[j][0..3]; lane i
+// receives M[4e + i/4][i%4] for e = 0..3.  With lane j pointing at
+// X[r0 + j/4][c0 + 4*(j%4)] of a row-major tile X, lane i receives
+// X[r0 + e][c0 + i], e = 0..3: four consecutive rows of one column.
+__device__ __forceinline__ shortx4 lds_read_tr4(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p));
+}
+
+template <typename V>
+__device__ __forceinline__ V join8(shortx4 lo, shortx4 hi) {
+    typedef short shortx8 __attribute__((ext_vector_type(8)));
+    const shortx8 x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(V, x);
+}
+
 // Workgroups are handed to the 8 XCDs round-robin (hardware id % 8).  Remap
 // so that consecutive logical ids run on the same XCD and share its L2:
 // hardware ids x, x+8, x+16, ... become one contiguous logical range.
@@ -56,23 +86,6 @@ __device__ __forceinline__ unsigned xcd_remap(unsigned id, unsigned total) {
     const unsigned per = total / kXcd, rem = total % kXcd;
     const unsigned x = id % kXcd, idx = id / kXcd;
     return x < rem ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
-}
-
-// Pack the 16-bit element e (0..7) of two 8-element rows into one dword:
-// low half from row a, high half from row b.
-template <int E>
-__device__ __forceinline__ uint32_t pack_col(u32x4 a, u32x4 b) {
-    const uint32_t x = a[E >> 1], y = b[E >> 1];
-    return (E & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-}
-
-// Row index within a 32-key block whose score lands in S^T accumulator row i
-// when K is fed as the A operand: swapping bits 2 and 3 makes accumulator
-// registers 0..7 of lane half h hold keys 8h..8h+7 and registers 8..15 keys
-// 16+8h..16+8h+7, which is exactly the contraction order the next MFMA
-// (O^T += V^T P^T) wants for its B operand.
-__device__ __forceinline__ int key_perm(int i) {
-    return (i & 0x13) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
 }  // namespace fa

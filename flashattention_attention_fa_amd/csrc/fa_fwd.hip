@@ -30,6 +30,8 @@
 //                 equal the B-operand layout), V^T is read from LDS where the
 //                 V tile was stored transposed.
 // Epilogue: O /= l, lse = (m + log2 l) * ln 2, both fp32.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -40,16 +42,17 @@ struct FwdTile {
     static constexpr int BM = 128;                // queries per workgroup
     static constexpr int BN = 64;                 // keys per tile
     static constexpr int THREADS = 256;
-    static constexpr int KLD = D + 8;             // K tile row stride (elements)
-    static constexpr int VLD = BN + 8;            // V^T tile row stride (elements)
+    static constexpr int LD = D + 8;              // K and V tile row stride (elements)
     static constexpr int KCH = D / 8;             // 16-byte chunks per row
-    static constexpr int K_LOADS = BN * KCH / THREADS;
-    static constexpr int V_GROUPS = (BN / 4) * KCH;   // 4 keys x 8 dims each
-    static constexpr int K_ELEMS = BN * KLD;
-    static constexpr int V_ELEMS = D * VLD;
-    static_assert(BN * KCH % THREADS == 0, "K tile must split evenly");
-    static_assert(V_GROUPS <= THREADS, "one V group per thread at most");
+    static constexpr int LOADS = BN * KCH / THREADS;   // per thread, per tensor, per tile
+    static constexpr int ELEMS = BN * LD;
+    static_assert(BN * KCH % THREADS == 0, "tile must split evenly over the threads");
 };
+
+// Rescale slack in log2 units: the running max m is only raised (and O, l
+// rescaled) when some query's tile max exceeds m by more than this, so the
+// unnormalised weights stay below 2^8 and fit bf16/fp16 with room to spare.
+constexpr float kRescaleSlack = 8.0f;
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
@@ -60,10 +63,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
     typedef FwdTile<D> C;
     typedef typename T::vec8 vec8;
     typedef typename T::scalar scalar;
-    constexpr int BM = C::BM, BN = C::BN;
+    constexpr int BM = C::BM, BN = C::BN, LD = C::LD;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::K_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][C::V_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][C::ELEMS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -84,66 +87,48 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
         qt = (int)(id % (unsigned)nq);
     }
     const size_t head = (size_t)bh * N * D;
-    const uint16_t *qh = q + head, *kh = k + head, *vh = v + head;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + head, head_bytes);
     const int q0 = qt * BM;
     const int qw = q0 + wave * 32;   // first query of this wave
     const int my_q = qw + li;
 
-    // Q fragments: B operand, lane (li, lh) holds row my_q, dims 16t+8lh..+8.
+    // Q fragments: B operand, lane (li, lh) holds row my_q, dims 16t+8lh..+8
+    // (rows past N read as zero).
     vec8 qf[D / 16];
-    {
-        const bool ok = my_q < N;
-        const uint16_t *src = qh + (size_t)(ok ? my_q : 0) * D + 8 * lh;
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-            u32x4 x = ok ? *(const u32x4 *)(src + 16 * t) : zero4();
-            // scale < 0: flip the sign of q (exact) and use |scale|;
-            // scale == 0: every visible score is 0, i.e. q = 0.
-            x = (x & qand) ^ qxor;
-            qf[t] = as_vec8<vec8>(x);
-        }
+    for (int t = 0; t < D / 16; ++t) {
+        u32x4 x = buffer_load16(qr, (uint32_t)(my_q * D + 16 * t + 8 * lh) * 2u);
+        // scale < 0: flip the sign of q (exact) and use |scale|;
+        // scale == 0: every visible score is 0, i.e. q = 0.
+        x = (x & qand) ^ qxor;
+        qf[t] = as_vec8<vec8>(x);
     }
 
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int ntiles = (kv_end + BN - 1) / BN;
 
-    u32x4 kreg[C::K_LOADS];
-    u32x4 vreg[4];
-
+    // Global -> register staging of one K and one V tile; rows past N read
+    // as zero (buffer range check), and are masked out of the softmax.
+    u32x4 kreg[C::LOADS], vreg[C::LOADS];
     auto load_tile = [&](int kv0) {
 #pragma unroll
-        for (int r = 0; r < C::K_LOADS; ++r) {
+        for (int r = 0; r < C::LOADS; ++r) {
             const int ch = tid + C::THREADS * r;
-            const int row = ch / C::KCH, col = ch % C::KCH;
-            const int key = kv0 + row;
-            kreg[r] = key < N ? *(const u32x4 *)(kh + (size_t)key * D + col * 8) : zero4();
-        }
-        if (tid < C::V_GROUPS) {
-            const int dc = tid % C::KCH, kg = tid / C::KCH;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = kv0 + 4 * kg + r;
-                vreg[r] = key < N ? *(const u32x4 *)(vh + (size_t)key * D + dc * 8) : zero4();
-            }
+            const uint32_t off = (uint32_t)((kv0 + ch / C::KCH) * D + (ch % C::KCH) * 8) * 2u;
+            kreg[r] = buffer_load16(kr, off);
+            vreg[r] = buffer_load16(vr, off);
         }
     };
-
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int r = 0; r < C::K_LOADS; ++r) {
+        for (int r = 0; r < C::LOADS; ++r) {
             const int ch = tid + C::THREADS * r;
-            const int row = ch / C::KCH, col = ch % C::KCH;
-            *(u32x4 *)&Ks[buf][row * C::KLD + col * 8] = kreg[r];
-        }
-        if (tid < C::V_GROUPS) {
-            const int dc = tid % C::KCH, kg = tid / C::KCH;
-            uint16_t *dst = &Vt[buf][(dc * 8) * C::VLD + 4 * kg];
-#define FA_VT_STORE(E)                                                        \
-    *(u32x2 *)(dst + (E) * C::VLD) =                                          \
-        u32x2{pack_col<E>(vreg[0], vreg[1]), pack_col<E>(vreg[2], vreg[3])};
-            FA_VT_STORE(0) FA_VT_STORE(1) FA_VT_STORE(2) FA_VT_STORE(3)
-            FA_VT_STORE(4) FA_VT_STORE(5) FA_VT_STORE(6) FA_VT_STORE(7)
-#undef FA_VT_STORE
+            const int idx = (ch / C::KCH) * LD + (ch % C::KCH) * 8;
+            *(u32x4 *)&Ks[buf][idx] = kreg[r];
+            *(u32x4 *)&Vs[buf][idx] = vreg[r];
         }
     };
 
@@ -158,35 +143,44 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
     store_tile(0);
     __syncthreads();
 
-    const int kp = key_perm(li);
-    for (int j = 0; j < ntiles; ++j) {
+    // ds_read_b64_tr_b16 addressing for the V^T operand: lane j of each
+    // 16-lane group points at row (j/4), column 16*(group&1) + 4*(j%4).
+    const int tr_row = (lane & 15) >> 2;
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    // One KV tile.  MASK is a compile-time flag so that interior tiles carry
+    // no per-element compare at all; only the diagonal tiles (causal) and the
+    // ragged last tile run the masked variant.
+    auto step = [&](int j, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int buf = j & 1;
         const int kv0 = j * BN;
         if (j + 1 < ntiles) load_tile(kv0 + BN);
 
         // Causal: a wave whose queries all precede the tile has nothing to do.
-        const bool active = !CAUSAL || kv0 <= qw + 31;
+        const bool active = !(CAUSAL && MASK) || kv0 <= qw + 31;
         if (active) {
+            // S^T = K Q^T: lane (li, lh), register r of block kb holds the
+            // score of query my_q against key kv0 + 32kb + 8(r/4) + 4lh + r%4.
             floatx16 s[BN / 32];
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-                const uint16_t *ka = &Ks[buf][(32 * kb + kp) * C::KLD + 8 * lh];
+                const uint16_t *ka = &Ks[buf][(32 * kb + li) * LD + 8 * lh];
 #pragma unroll
                 for (int t = 0; t < D / 16; ++t)
                     s[kb] = T::mfma32(as_vec8<vec8>(*(const u32x4 *)(ka + 16 * t)), qf[t], s[kb]);
             }
 
-            // Mask keys past the end and, on diagonal tiles, keys after the query.
-            const bool need_mask = (kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > qw);
-            if (need_mask) {
+            if constexpr (MASK) {
+                // keys past the end, and (causal) keys after the query
                 const int lim = CAUSAL ? min(N - 1, my_q) : N - 1;
 #pragma unroll
                 for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = kv0 + 32 * kb + 16 * (r >> 3) + 8 * lh + (r & 7);
+                        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
                         if (key > lim) s[kb][r] = -INFINITY;
                     }
             }
@@ -197,15 +191,18 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
             mx = fmaxf(mx, other_half(mx));
-            const float m_new = fmaxf(m_run, mx * c);
-            const float mb = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - mb);
-            m_run = m_new;
-            l_run *= alpha;
+            const float mt = mx * c;
+            if (__any(mt > m_run + kRescaleSlack)) {
+                const float m_new = fmaxf(m_run, mt);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+                for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            }
+            const float mb = m_run == -INFINITY ? 0.f : m_run;
 
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb)
@@ -216,6 +213,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
                     l_run += p;
                 }
 
+            // O^T += V^T P^T.  MFMA u of key block kb contracts over keys
+            // 32kb + 16u + 8(e/4) + 4lh + e%4 (e = 0..7): P^T is registers
+            // 8u..8u+7 of s[kb]; V^T comes from two transposing reads of 4
+            // keys each.
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
@@ -223,17 +224,27 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
                     vec8 pb;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) pb[e] = (scalar)s[kb][8 * u + e];
-                    const uint16_t *va = &Vt[buf][li * C::VLD + 32 * kb + 16 * u + 8 * lh];
+                    const uint16_t *va = &Vs[buf][(32 * kb + 16 * u + 4 * lh + tr_row) * LD + tr_col];
 #pragma unroll
-                    for (int db = 0; db < D / 32; ++db)
-                        oacc[db] = T::mfma32(
-                            as_vec8<vec8>(*(const u32x4 *)(va + 32 * db * C::VLD)), pb, oacc[db]);
+                    for (int db = 0; db < D / 32; ++db) {
+                        const vec8 vt = join8<vec8>(lds_read_tr4(va + 32 * db),
+                                                    lds_read_tr4(va + 8 * LD + 32 * db));
+                        oacc[db] = T::mfma32(vt, pb, oacc[db]);
+                    }
                 }
         }
 
         if (j + 1 < ntiles) store_tile(buf ^ 1);
         __syncthreads();
-    }
+    };
+
+    // Tiles before n_full need no mask for any query of the workgroup: all
+    // their keys exist and (causal) precede the workgroup's first query.
+    int n_full = N / BN;
+    if (CAUSAL) n_full = min(n_full, q0 / BN);
+    n_full = min(n_full, ntiles);
+    for (int j = 0; j < n_full; ++j) step(j, std::false_type{});
+    for (int j = n_full; j < ntiles; ++j) step(j, std::true_type{});
 
     // Epilogue.  O^T accumulator: lane (li, lh), register r of block db holds
     // dim 32*db + 8*(r/4) + 4*lh + r%4 of query my_q.

@@ -53,7 +53,7 @@ typedef enum { FA_BF16 = 0, FA_FP16 = 1 } fa_dtype_t;
  *   q, k, v : [B, H, N, d] 16-bit (dtype), device, 16-byte aligned
  *   o       : [B, H, N, d] fp32, device, 16-byte aligned (written)
  *   lse     : [B, H, N]    fp32, device, 4-byte aligned, or NULL to skip
- *   d       : 64 or 128
+ *   d       : 64 or 128;  N <= 2^23 (else FA_ERR_SHAPE)
  *   scale   : finite; 1/sqrt(d) reproduces the usual default
  * B == 0, H == 0 or N == 0 is a no-op returning FA_OK.
  */
@@ -75,7 +75,7 @@ fa_status_t fa_fwd(const void *q, const void *k, const void *v, float *o,
  *   q              : [B, Hq, d]       16-bit, device, 16-byte aligned
  *   kcache, vcache : [B, Hkv, L, d]   16-bit, device, 16-byte aligned
  *   o              : [B, Hq, d]       fp32, device, 16-byte aligned (written)
- *   Hq % Hkv == 0; L >= 1; nsplit >= 1 (clamped to L; shard s covers keys
+ *   Hq % Hkv == 0; 1 <= L <= 2^23; nsplit >= 1 (clamped to L; shard s covers keys
  *   [s*C, min(L, (s+1)*C)) with C = ceil(L / nsplit)).
  * Partial results live in a per-device workspace that the library allocates
  * on first use and grows when a larger call needs it (guarded by a mutex;

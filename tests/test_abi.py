@@ -49,7 +49,7 @@ def test_fwd_validation(L):
     assert fwd(L, lse=A + 2) == ALIGN
     assert fwd(L, scale=float("nan")) == VALUE
     assert fwd(L, scale=float("inf")) == VALUE
-    assert fwd(L, N=(1 << 30) + 1) == SHAPE
+    assert fwd(L, N=(1 << 23) + 1) == SHAPE
     assert fwd(L, B=65536, H=65536) == SHAPE
 
 
@@ -82,6 +82,7 @@ def test_decode_validation(L):
     assert dec(L, dtype=3) == UNSUP
     assert dec(L, k=MIS) == ALIGN
     assert dec(L, B=70000) == SHAPE
+    assert dec(L, Lk=(1 << 23) + 1) == SHAPE
     assert dec(L, q=None, B=0) == OK
     assert dec(L, q=None, Hq=0) == OK
 
