@@ -300,11 +300,13 @@ __global__ __launch_bounds__(128) void fa_decode_combine_kernel(
         for (int s = tid; s < n; s += 128)
             w[s] = total == -INFINITY ? 0.f : expf(pl[s0 + s] - total);
         __syncthreads();
-        if (tid < D)
-            for (int s = 0; s < n; ++s) {
-                const float ww = w[s];
-                if (ww > 0.f) acc += ww * po[(size_t)(s0 + s) * D + tid];
-            }
+        // No branch on the weight: shards without keys hold O_s = 0 and
+        // weight 0, and a branch-free loop lets the loads issue together.
+        if (tid < D) {
+            const float *pp = po + (size_t)s0 * D + tid;
+#pragma unroll 8
+            for (int s = 0; s < n; ++s) acc += w[s] * pp[(size_t)s * D];
+        }
         __syncthreads();
     }
     if (tid < D) o[row * D + tid] = acc;

@@ -42,10 +42,16 @@ struct FwdTile {
     static constexpr int BM = 128;                // queries per workgroup
     static constexpr int BN = 64;                 // keys per tile
     static constexpr int THREADS = 256;
-    static constexpr int LD = D + 8;              // K and V tile row stride (elements)
+    // LDS row strides (elements).  K rows are read 16 bytes per lane, 32
+    // consecutive rows per instruction; V rows are read by the transposing
+    // read, 4 rows x 32 bytes per 16 lanes.  The paddings keep both patterns
+    // free of bank conflicts.
+    static constexpr int LDK = D + 8;
+    static constexpr int LDV = D + 32;
     static constexpr int KCH = D / 8;             // 16-byte chunks per row
     static constexpr int LOADS = BN * KCH / THREADS;   // per thread, per tensor, per tile
-    static constexpr int ELEMS = BN * LD;
+    static constexpr int K_ELEMS = BN * LDK;
+    static constexpr int V_ELEMS = BN * LDV;
     static_assert(BN * KCH % THREADS == 0, "tile must split evenly over the threads");
 };
 
@@ -63,10 +69,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
     typedef FwdTile<D> C;
     typedef typename T::vec8 vec8;
     typedef typename T::scalar scalar;
-    constexpr int BM = C::BM, BN = C::BN, LD = C::LD;
+    constexpr int BM = C::BM, BN = C::BN, LDK = C::LDK, LDV = C::LDV;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][C::ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][C::V_ELEMS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -74,18 +80,13 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
     const int li = lane & 31;   // query column inside the wave's 32
     const int lh = lane >> 5;   // lane half
 
-    // Block -> (q-tile, head).  Non-causal: consecutive logical ids walk the
-    // q-tiles of one head (K/V stay hot in that XCD's L2).  Causal: the
-    // longest q-tiles (most keys) start first.
+    // Block -> (head, q-tile).  Consecutive logical ids walk the q-tiles of
+    // one head, so the workgroups resident on one XCD share that head's K/V
+    // in their L2.  Causal: each head's q-tiles run longest (most keys) first,
+    // so the short ones fill the tail.
     const unsigned id = xcd_remap(blockIdx.x, gridDim.x);
-    int qt, bh;
-    if (CAUSAL) {
-        qt = nq - 1 - (int)(id / (unsigned)BH);
-        bh = (int)(id % (unsigned)BH);
-    } else {
-        bh = (int)(id / (unsigned)nq);
-        qt = (int)(id % (unsigned)nq);
-    }
+    const int bh = (int)(id / (unsigned)nq);
+    const int qt = CAUSAL ? nq - 1 - (int)(id % (unsigned)nq) : (int)(id % (unsigned)nq);
     const size_t head = (size_t)bh * N * D;
     const uint32_t head_bytes = (uint32_t)N * D * 2;
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + head, head_bytes);
@@ -126,9 +127,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
 #pragma unroll
         for (int r = 0; r < C::LOADS; ++r) {
             const int ch = tid + C::THREADS * r;
-            const int idx = (ch / C::KCH) * LD + (ch % C::KCH) * 8;
-            *(u32x4 *)&Ks[buf][idx] = kreg[r];
-            *(u32x4 *)&Vs[buf][idx] = vreg[r];
+            const int row = ch / C::KCH, col = (ch % C::KCH) * 8;
+            *(u32x4 *)&Ks[buf][row * LDK + col] = kreg[r];
+            *(u32x4 *)&Vs[buf][row * LDV + col] = vreg[r];
         }
     };
 
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
             for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-                const uint16_t *ka = &Ks[buf][(32 * kb + li) * LD + 8 * lh];
+                const uint16_t *ka = &Ks[buf][(32 * kb + li) * LDK + 8 * lh];
 #pragma unroll
                 for (int t = 0; t < D / 16; ++t)
                     s[kb] = T::mfma32(as_vec8<vec8>(*(const u32x4 *)(ka + 16 * t)), qf[t], s[kb]);
@@ -224,11 +225,11 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
                     vec8 pb;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) pb[e] = (scalar)s[kb][8 * u + e];
-                    const uint16_t *va = &Vs[buf][(32 * kb + 16 * u + 4 * lh + tr_row) * LD + tr_col];
+                    const uint16_t *va = &Vs[buf][(32 * kb + 16 * u + 4 * lh + tr_row) * LDV + tr_col];
 #pragma unroll
                     for (int db = 0; db < D / 32; ++db) {
                         const vec8 vt = join8<vec8>(lds_read_tr4(va + 32 * db),
-                                                    lds_read_tr4(va + 8 * LD + 32 * db));
+                                                    lds_read_tr4(va + 8 * LDV + 32 * db));
                         oacc[db] = T::mfma32(vt, pb, oacc[db]);
                     }
                 }
