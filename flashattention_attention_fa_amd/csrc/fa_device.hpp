@@ -26,19 +26,35 @@ constexpr float kLn2 = 0.6931471805599453f;
 // (column = lane%32); lanes 32..63 hold the second half of the 16-wide
 // contraction.  C: lane%32 is the column, register r of lane half h is row
 // 8*(r/4) + 4*h + r%4.
+//
+// sum8(p, l): l + the sum of the 8 rounded weights in p, or nothing (kSumP
+// false) when the row sum must be taken from the fp32 weights instead: a
+// bf16 weight carries up to 2^-9 relative rounding error, too much for the
+// log-sum-exp, while fp16's 2^-11 is not.
 struct BF16 {
     typedef bf16x8 vec8;
     typedef __bf16 scalar;
+    static constexpr bool kSumP = false;
     static __device__ __forceinline__ floatx16 mfma32(vec8 a, vec8 b, floatx16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    static __device__ __forceinline__ float sum8(vec8, float l) { return l; }
 };
 
 struct FP16 {
     typedef f16x8 vec8;
     typedef _Float16 scalar;
+    static constexpr bool kSumP = true;
     static __device__ __forceinline__ floatx16 mfma32(vec8 a, vec8 b, floatx16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float sum8(vec8 p, float l) {
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            l = __builtin_amdgcn_fdot2(f16x2{p[2 * i], p[2 * i + 1]}, one, l, false);
+        return l;
     }
 };
 
@@ -61,6 +77,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
 }
+
+// Direct global -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane i of the wave writes lds_base + 16*i; out-of-range reads store zeros.
+// The LDS destination must be wave-uniform.  Completion is tracked by the
+// vector-memory counter, like any load.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                                  uint16_t *lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)lds_base, 16, (int)byte_off, 0, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory operations (including
+// direct-to-LDS copies) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane
 // j supplies the address of 4 consecutive 16-bit elements M[j][0..3]; lane i
