@@ -43,10 +43,9 @@ namespace fa {
 
 template <int D>
 struct FwdTile {
-    static constexpr int QB = 2;                  // 32-query blocks per wave
-    static constexpr int BM = 4 * 32 * QB;        // queries per workgroup
-    static constexpr int BN = 32;                 // keys per tile
-    static constexpr int KB = BN / 32;            // 32-key blocks per tile
+    static constexpr int BM = 128;                // queries per workgroup (32 per wave)
+    static constexpr int KB = 2;                  // 32-key blocks per tile
+    static constexpr int BN = 32 * KB;            // keys per tile
     static constexpr int THREADS = 256;
     static constexpr int KCH = D / 8;             // 16-byte chunks per row
     static constexpr int RPI = 64 / KCH;          // rows one wave copy instruction covers
@@ -96,17 +95,16 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fa_fwd_kernel(
+__global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, float *__restrict__ o,
     float *__restrict__ lse, int N, int nq, float c, uint32_t qand, uint32_t qxor) {
     typedef FwdTile<D> C;
     typedef typename T::vec8 vec8;
     typedef typename T::scalar scalar;
-    constexpr int QB = C::QB, BM = C::BM, BN = C::BN, KCH = C::KCH;
-    constexpr int KSTEPS = D / 16;         // QK^T MFMAs per 32-query block and tile
+    constexpr int BM = C::BM, BN = C::BN, KB = C::KB, KCH = C::KCH;
+    constexpr int KSTEPS = D / 16;         // QK^T MFMAs per 32-key block
     constexpr int DB = D / 32;             // 32-dim blocks of O
-    static_assert(BN == 32 && QB == 2, "the schedule below is written for 32-key tiles");
 
     // Two K and two V tile buffers, each its own LDS object: every access
     // below names its buffer at compile time, so the compiler can tell that
@@ -119,7 +117,7 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int li = lane & 31;   // query column inside a 32-query block
+    const int li = lane & 31;   // query column inside the wave's 32
     const int lh = lane >> 5;   // lane half
 
     // Block -> (head, q-tile).  Consecutive logical ids walk the q-tiles of
@@ -135,24 +133,20 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_kernel(
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + head, head_bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + head, head_bytes);
     const int q0 = qt * BM;
-    const int qw = q0 + wave * 32 * QB;   // first query of this wave
+    const int qw = q0 + wave * 32;    // first query of this wave
+    const int my_q = qw + li;
 
-    // Q fragments: B operand, lane (li, lh) of block qb holds query
-    // qw + 32qb + li, dims 16t+8lh..+8 (rows past N read as zero).
-    vec8 qf[QB][KSTEPS];
+    // Q fragments: B operand, lane (li, lh) holds query my_q, dims
+    // 16t+8lh..+8 (rows past N read as zero).
+    vec8 qf[KSTEPS];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-            u32x4 x = buffer_load16(qr, (uint32_t)((qw + 32 * qb + li) * D + 16 * t + 8 * lh) * 2u);
-            // scale < 0: flip the sign of q (exact) and use |scale|;
-            // scale == 0: every visible score is 0, i.e. q = 0.
-            x = (x & qand) ^ qxor;
-            qf[qb][t] = as_vec8<vec8>(x);
-            // Q is only ever an MFMA operand: keep it in accumulation
-            // registers and leave the vector registers to S, P and operands.
-            asm volatile("" : "+a"(qf[qb][t]));
-        }
+    for (int t = 0; t < KSTEPS; ++t) {
+        u32x4 x = buffer_load16(qr, (uint32_t)(my_q * D + 16 * t + 8 * lh) * 2u);
+        // scale < 0: flip the sign of q (exact) and use |scale|;
+        // scale == 0: every visible score is 0, i.e. q = 0.
+        x = (x & qand) ^ qxor;
+        qf[t] = as_vec8<vec8>(x);
+    }
 
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int ntiles = (kv_end + BN - 1) / BN;
@@ -171,25 +165,28 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_kernel(
         koff[i] = (uint32_t)(row * D + 8 * (pos ^ swz_k<D>(row))) * 2u;
         voff[i] = (uint32_t)(row * D + 8 * (pos ^ swz_v<D>(row))) * 2u;
     }
-    auto load_tiles = [&](int ktile, uint16_t *kbuf, int vtile, uint16_t *vbuf)
-        __attribute__((always_inline)) {
+    auto load_k = [&](int tile, uint16_t *buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) {
-            const int dst = (wave * (BN / 4) + i * C::RPI) * D;
-            buffer_load16_lds(kr, koff[i] + (uint32_t)ktile * (BN * D * 2), kbuf + dst);
-            buffer_load16_lds(vr, voff[i] + (uint32_t)vtile * (BN * D * 2), vbuf + dst);
-        }
+        for (int i = 0; i < C::LOADS; ++i)
+            buffer_load16_lds(kr, koff[i] + (uint32_t)tile * (BN * D * 2),
+                              buf + (wave * (BN / 4) + i * C::RPI) * D);
+    };
+    auto load_v = [&](int tile, uint16_t *buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i)
+            buffer_load16_lds(vr, voff[i] + (uint32_t)tile * (BN * D * 2),
+                              buf + (wave * (BN / 4) + i * C::RPI) * D);
     };
 
-    // K operand: logical chunk 2t + lh of row li (swizzled).
+    // K operand of block kb, step t: logical chunk 2t + lh of row 32kb + li.
     int kcol[KSTEPS];
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) kcol[t] = li * D + 8 * ((2 * t + lh) ^ swz_k<D>(li));
-    auto read_k = [&](const uint16_t *buf, int t) __attribute__((always_inline)) {
-        return as_vec8<vec8>(*(const u32x4 *)(buf + kcol[t]));
+    auto read_k = [&](const uint16_t *buf, int kb, int t) __attribute__((always_inline)) {
+        return as_vec8<vec8>(*(const u32x4 *)(buf + 32 * kb * D + kcol[t]));
     };
-    // V^T operand of PV MFMA u, dim block db, by two transposing reads: lane
-    // j of each 16-lane group points at row 16u + 4lh + j/4 (+8 for the
+    // V^T operand of PV MFMA (kb, u, db) by two transposing reads: lane j of
+    // each 16-lane group points at row 32kb + 16u + 4lh + j/4 (+8 for the
     // second read) and logical column 32db + 16*(group&1) + 4*(j%4).  The
     // row swizzle is the same for all those rows.
     const int tr_row = 4 * lh + ((lane & 15) >> 2);
@@ -199,109 +196,80 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_kernel(
         const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
         vcol[db] = tr_row * D + 8 * ((col >> 3) ^ swz_v<D>(tr_row)) + (col & 7);
     }
-    auto read_v = [&](const uint16_t *buf, int u, int db) __attribute__((always_inline)) {
-        const uint16_t *p = buf + 16 * u * D + vcol[db];
+    auto read_v = [&](const uint16_t *buf, int kb, int u, int db) __attribute__((always_inline)) {
+        const uint16_t *p = buf + (32 * kb + 16 * u) * D + vcol[db];
         return join8<vec8>(lds_read_tr4(p), lds_read_tr4(p + 8 * D));
     };
 
-    floatx16 oacc[QB][DB];
+    floatx16 oacc[DB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
-    float m_run[QB], l_run[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m_run[qb] = -INFINITY;
-        l_run[qb] = 0.f;
-    }
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
     const floatx16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
                              0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
     // S^T of one tile, two register sets used alternately (tile parity):
-    // lane (li, lh), register r of block qb holds the score of query
-    // qw + 32qb + li against key tile*BN + 8(r/4) + 4lh + r%4.
-    floatx16 sA[QB], sB[QB];
+    // lane (li, lh), register r of block kb holds the score of query my_q
+    // against key tile*BN + 32kb + 8(r/4) + 4lh + r%4.
+    floatx16 sA[KB], sB[KB];
 
     // Keys past the end and (causal) keys after the query get -inf.
-    auto mask = [&](floatx16 (&x)[QB], int tile) __attribute__((always_inline)) {
+    auto mask = [&](floatx16 (&x)[KB], int tile) __attribute__((always_inline)) {
         const int kv0 = tile * BN;
+        const int lim = CAUSAL ? min(N - 1, my_q) : N - 1;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int my_q = qw + 32 * qb + li;
-            const int lim = CAUSAL ? min(N - 1, my_q) : N - 1;
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = kv0 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (key > lim) x[qb][r] = -INFINITY;
+                const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (key > lim) x[kb][r] = -INFINITY;
             }
-        }
     };
-    // Row maxima of a tile, in log2 units.
-    float mt[QB];
-    // (maximum, not fmaxf: no NaN can occur here, and maximum maps straight
-    // onto v_maximum3_f32 without canonicalising every MFMA result first.)
-    auto row_max = [&](const floatx16 (&x)[QB], int qb) __attribute__((always_inline)) {
-        float mx = __builtin_elementwise_maximum(x[qb][0], x[qb][1]);
+    // Row maximum of a tile in log2 units.  (maximum, not fmaxf: no NaN can
+    // occur here, and maximum maps onto v_maximum3_f32 without
+    // canonicalising every MFMA result first.)
+    float mt = 0.f;
+    auto row_max = [&](const floatx16 (&x)[KB]) __attribute__((always_inline)) {
+        float mx = __builtin_elementwise_maximum(x[0][0], x[0][1]);
 #pragma unroll
-        for (int r = 2; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, x[qb][r]);
-        mt[qb] = max_halves(mx) * c;
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = kb == 0 ? 2 : 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, x[kb][r]);
+        mt = max_halves(mx) * c;
     };
-    // Raise m (and rescale O, l) only when a tile max passes the slack.
+    // Raise m (and rescale O, l) only when the tile max passes the slack.
     auto raise_max = [&]() __attribute__((always_inline)) {
-        bool need = false;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) need |= mt[qb] > m_run[qb] + kRescaleSlack;
-        if (__any(need)) {
+        if (__any(mt > m_run + kRescaleSlack)) {
             // Rare path: keep it a real branch (the compiler would otherwise
             // turn it into unconditional multiplies of the whole O tile).
             asm volatile("" ::: "memory");
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float m_new = fmaxf(m_run[qb], mt[qb]);
-                const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-                m_run[qb] = m_new;
-                l_run[qb] *= alpha;
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
-            }
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
     };
 
-    // P^T operands: register r of block qb becomes element r%8 of operand
-    // pb[qb][r/8]; MFMA u contracts over keys 8(e/4) + 4lh + e%4 + 16u.
-    vec8 pb[QB][2];
-    float mb[QB];
-    auto softmax_part = [&](const floatx16 (&x)[QB], int qb, int r0, int n)
-        __attribute__((always_inline)) {
-#pragma unroll
-        for (int r = r0; r < r0 + n; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(x[qb][r], c, -mb[qb]));
-            if constexpr (!T::kSumP) l_run[qb] += p;
-            pb[qb][r >> 3][r & 7] = (scalar)p;
-        }
-    };
-    auto sum_p = [&](int qb, int u) __attribute__((always_inline)) {
-        if constexpr (T::kSumP) l_run[qb] = T::sum8(pb[qb][u], l_run[qb]);
-    };
+    // P^T operands: register r of block kb becomes element r%8 of operand
+    // pb[kb][r/8]; PV MFMA (kb, u) contracts over keys
+    // 32kb + 16u + 8(e/4) + 4lh + e%4.
+    vec8 pb[KB][2];
     // m is finite from tile 0 on (every query sees key 0), so the softmax
     // needs no guard against an infinite base.
-    auto set_mb = [&]() __attribute__((always_inline)) {
+    auto softmax_part = [&](const floatx16 (&x)[KB], int kb, int u) __attribute__((always_inline)) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) mb[qb] = m_run[qb];
-    };
-    auto pin_o = [&]() __attribute__((always_inline)) {
-        // O is only touched by the PV MFMAs (and the rare rescale): keep it in
-        // accumulation registers, so that those MFMAs accumulate there and
-        // the vector registers hold S, P and the operands in flight.
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(oacc[qb][db]));
+        for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(x[kb][8 * u + e], c, -m_run));
+            if constexpr (!T::kSumP) l_run += p;
+            pb[kb][u][e] = (scalar)p;
+        }
+        if constexpr (T::kSumP) l_run = T::sum8(pb[kb][u], l_run);
     };
 
     // Tiles before n_full need no mask for any query of the workgroup: all
@@ -311,38 +279,32 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_kernel(
     n_full = min(n_full, ntiles);
 
     // Prologue: K(0), K(1), V(0) into LDS; scores and maxima of tile 0.
-    load_tiles(0, K0, 0, V0);
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
-        buffer_load16_lds(kr, koff[i] + (uint32_t)(BN * D * 2), K1 + (wave * (BN / 4) + i * C::RPI) * D);
+    load_k(0, K0);
+    load_v(0, V0);
+    load_k(1, K1);
     wait_vmem();
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
-        const vec8 a = read_k(K0, t);
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sA[qb] = T::mfma32(a, qf[qb][t], t == 0 ? zero16 : sA[qb]);
-    }
+        for (int t = 0; t < KSTEPS; ++t)
+            sA[kb] = T::mfma32(read_k(K0, kb, t), qf[t], t == 0 ? zero16 : sA[kb]);
     if (n_full == 0) mask(sA, 0);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) row_max(sA, qb);
+    row_max(sA);
     raise_max();
     // Iteration 0 overwrites K0; every wave must be done reading K(0).
     __syncthreads();
 
-    // Iteration j (parity PAR = j % 2): softmax of tile j and QK^T of tile
-    // j+1, then PV of tile j and the row maxima of tile j+1.  LDS holds K(j+1)
-    // in K[1-PAR] and V(j) in V[PAR]; K(j+2) and V(j+1) are copied meanwhile
-    // into K[PAR] and V[1-PAR], which iteration j-1 finished reading, and the
-    // barrier at the end publishes them.
-    //
-    // The instruction order is spelled out and fenced with sched_barrier:
-    // with one wave per SIMD, the matrix core only stays busy if every MFMA
-    // is issued next to independent vector work (the softmax of the previous
-    // tile, the row maxima of the next) and its operands were requested from
-    // LDS well before.
-    auto iteration = [&](int j, auto par, auto mask_tag, floatx16 (&cur)[QB],
-                         floatx16 (&nxt)[QB]) __attribute__((always_inline)) {
+    // Iteration j (parity PAR = j % 2): softmax of tile j next to QK^T of
+    // tile j+1, then PV of tile j next to the row maximum of tile j+1.  LDS
+    // holds K(j+1) in K[1-PAR] and V(j) in V[PAR]; K(j+2) and V(j+1) are
+    // copied meanwhile into K[PAR] and V[1-PAR], which iteration j-1 finished
+    // reading, and the barrier at the end publishes them.  Two waves share
+    // each SIMD, so one wave's softmax overlaps the other's MFMAs; the order
+    // below additionally gives every wave independent work next to each
+    // MFMA.  Phase boundaries are fenced so the compiler keeps that order.
+    auto iteration = [&](int j, auto par, auto mask_tag, floatx16 (&cur)[KB],
+                         floatx16 (&nxt)[KB]) __attribute__((always_inline)) {
         constexpr bool MASK_NEXT = decltype(mask_tag)::value;
         constexpr int PAR = decltype(par)::value;
         uint16_t *const kb_next = PAR ? K0 : K1;   // holds K(j+1)
@@ -350,52 +312,31 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_kernel(
         uint16_t *const vb_cur = PAR ? V1 : V0;    // holds V(j)
         uint16_t *const vb_fill = PAR ? V0 : V1;   // receives V(j+1)
 
-        vec8 kop[KSTEPS];
+        load_k(j + 2, kb_fill);
+        load_v(j + 1, vb_fill);
+        // Phase 1: QK^T(j+1) | softmax(j) of key block 0.
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) kop[t] = read_k(kb_next, t);
-        load_tiles(j + 2, kb_fill, j + 1, vb_fill);
-        set_mb();
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int t = 0; t < KSTEPS; ++t) {
+                nxt[kb] = T::mfma32(read_k(kb_next, kb, t), qf[t], t == 0 ? zero16 : nxt[kb]);
+                if (kb == 0 && t == 1) softmax_part(cur, 0, 0);
+                if (kb == 0 && t == KSTEPS / 2 + 1) softmax_part(cur, 0, 1);
+                if (KB > 1 && kb == 1 && t == 1) softmax_part(cur, KB - 1, 0);
+            }
         __builtin_amdgcn_sched_barrier(0);
-
-        // Phase 1: QK^T(j+1) | first half of softmax(j) (P operand u = 0) |
-        // V^T(j) reads.
-        vec8 vop[2][DB];
-        constexpr int PER_STEP = 2 * 8 / KSTEPS;    // u = 0 elements per QK step
-#pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-                nxt[qb] = T::mfma32(kop[t], qf[qb][t], t == 0 ? zero16 : nxt[qb]);
-            const int e0 = t * PER_STEP;            // over (qb, r < 8)
-            softmax_part(cur, e0 / 8, e0 % 8, PER_STEP);
-            vop[t / DB][t % DB] = read_v(vb_cur, t / DB, t % DB);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // Phase 2a: PV(j) over keys 0..15 | second half of softmax(j).
-        constexpr int PER_DB = 2 * 8 / DB;           // u = 1 elements per PV step
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-                oacc[qb][db] = T::mfma32(vop[0][db], pb[qb][0], oacc[qb][db]);
-            const int e0 = db * PER_DB;             // over (qb, 8 <= r < 16)
-            softmax_part(cur, e0 / 8, 8 + e0 % 8, PER_DB);
-            if (db < QB) sum_p(db, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // Phase 2b: PV(j) over keys 16..31 | row maxima of tile j+1.
+        // Phase 2: PV(j) | rest of softmax(j) | row maximum of tile j+1.
+        if constexpr (KB > 1) softmax_part(cur, KB - 1, 1);
         if constexpr (MASK_NEXT) mask(nxt, j + 1);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-                oacc[qb][db] = T::mfma32(vop[1][db], pb[qb][1], oacc[qb][db]);
-            if (db < QB) sum_p(db, 1), row_max(nxt, db);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        pin_o();
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    oacc[db] = T::mfma32(read_v(vb_cur, kb, u, db), pb[kb][u], oacc[db]);
+        row_max(nxt);
+        __builtin_amdgcn_sched_barrier(0);
         raise_max();
         wait_vmem();
         __syncthreads();
@@ -416,45 +357,34 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_kernel(
     run(split, ntiles - 1, std::true_type{});
 
     // Last tile: softmax and PV only.
-    auto last = [&](floatx16 (&cur)[QB], const uint16_t *vb) __attribute__((always_inline)) {
-        set_mb();
+    auto last = [&](floatx16 (&cur)[KB], const uint16_t *vb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            softmax_part(cur, qb, 0, 16);
-            sum_p(qb, 0);
-            sum_p(qb, 1);
-        }
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < 2; ++u) {
+                softmax_part(cur, kb, u);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const vec8 vt = read_v(vb, u, db);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    oacc[qb][db] = T::mfma32(vt, pb[qb][u], oacc[qb][db]);
+                for (int db = 0; db < DB; ++db)
+                    oacc[db] = T::mfma32(read_v(vb, kb, u, db), pb[kb][u], oacc[db]);
             }
     };
     if ((ntiles - 1) & 1) last(sB, V1); else last(sA, V0);
 
     // Epilogue.  O^T accumulator: lane (li, lh), register r of block db holds
-    // dim 32*db + 8*(r/4) + 4*lh + r%4 of query qw + 32qb + li.
+    // dim 32*db + 8*(r/4) + 4*lh + r%4 of query my_q.
+    const float l_tot = sum_halves(l_run);
+    if (my_q < N) {
+        const float inv = 1.f / l_tot;
+        float *orow = o + head + (size_t)my_q * D + 4 * lh;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int my_q = qw + 32 * qb + li;
-        const float l_tot = sum_halves(l_run[qb]);
-        if (my_q < N) {
-            const float inv = 1.f / l_tot;
-            float *orow = o + head + (size_t)my_q * D + 4 * lh;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-                    *(floatx4 *)(orow + 32 * db + 8 * a) =
-                        floatx4{oacc[qb][db][4 * a] * inv, oacc[qb][db][4 * a + 1] * inv,
-                                oacc[qb][db][4 * a + 2] * inv, oacc[qb][db][4 * a + 3] * inv};
-            if (lse != nullptr && lh == 0)
-                lse[(size_t)bh * N + my_q] = (m_run[qb] + log2f(l_tot)) * kLn2;
-        }
+            for (int a = 0; a < 4; ++a)
+                *(floatx4 *)(orow + 32 * db + 8 * a) =
+                    floatx4{oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv,
+                            oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv};
+        if (lse != nullptr && lh == 0)
+            lse[(size_t)bh * N + my_q] = (m_run + log2f(l_tot)) * kLn2;
     }
 }
 
