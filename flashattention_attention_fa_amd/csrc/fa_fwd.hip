@@ -6,21 +6,20 @@
 // The running-max / running-sum rescaling is the "online normalisation"
 // the smzdm digest (section 6) tells multi-GPU users to check first.
 //
-// Work split: one workgroup = 4 waves = 256 queries of one (batch, head);
-// each wave owns 64 queries as two 32-query blocks, so every K or V operand
-// read from LDS feeds two MFMAs (LDS traffic per flop is what limits a
-// 32-query wave on this chip).  Keys stream through LDS in tiles of 64: the
-// K and V tiles of the coming iterations are copied from global memory
-// straight into the LDS buffers that just became free while the current tile
-// is computed (one barrier per tile).
+// Work split: one workgroup = 4 waves = 128 queries of one (batch, head);
+// each wave owns 32 queries.  Two workgroups share a compute unit, so every
+// SIMD runs two waves (at most 256 registers each): while one wave computes
+// exponentials the other keeps the matrix core busy.  Keys stream through
+// LDS in tiles of 64: the K and V tiles of the coming iterations are copied
+// from global memory straight into the LDS buffers that just became free
+// while the current tile is computed (one barrier per tile).
 //
-// The loop is software pipelined inside each wave (the pages contrast this
-// "different iterations of one role" schedule with warp specialisation):
-// iteration j issues the QK^T MFMAs of tile j+1 next to the exponentials of
-// tile j, then the PV MFMAs of tile j next to the row maxima of tile j+1, so
-// the matrix cores and the vector ALUs always have independent work.
+// The loop is also software pipelined inside each wave (the pages contrast
+// this "different iterations of one role" schedule with warp
+// specialisation): iteration j issues the QK^T MFMAs of tile j+1 next to the
+// exponentials of tile j, then the PV MFMAs of tile j.
 //
-// Per wave and tile (64 queries x 64 keys), for each 32-query block:
+// Per wave and tile (32 queries x 64 keys):
 //   S^T = K Q^T   MFMA 32x32x16; Q lives in registers for the whole loop
 //                 (B operand), K rows come from LDS (A operand).  Each lane
 //                 owns the scores of ONE query (its column): row max and row
@@ -28,8 +27,11 @@
 //   online softmax in the exp2 domain with c = scale*log2(e):
 //                 m' = max(m, c*max_j s_j);  alpha = 2^(m - m');
 //                 p_j = 2^(c*s_j - m');  l = alpha*l + sum p_j;  O *= alpha
-//                 (m is only raised when the tile max exceeds it by more than
-//                 a slack, which skips most O rescales exactly)
+//                 m is taken exactly from the first tile; later tiles keep it
+//                 unless their weights, computed with it, grow past a bound
+//                 (then m, O and l are updated as above and the tile's
+//                 weights recomputed).  Any m that keeps the weights finite
+//                 gives the same O and lse; the bound keeps them small.
 //   O^T += V^T P^T  P^T is the S^T accumulator converted to 16 bits in
 //                 place; V^T comes from the row-major V tile through the
 //                 transposing LDS read.
@@ -76,10 +78,14 @@ __device__ __forceinline__ int swz_v(int r) {
     return 4 * ((r / C::ROWS_PER_LINE) % (C::KCH / 4));
 }
 
-// Rescale slack in log2 units: the running max m is only raised (and O, l
-// rescaled) when some query's tile max exceeds m by more than this, so the
-// unnormalised weights stay below 2^8 and fit bf16/fp16 with room to spare.
-constexpr float kRescaleSlack = 8.0f;
+// Bound on one lane's sum of the unnormalised weights of a tile.  The running
+// max m is taken exactly from the first tile and afterwards only raised when a
+// tile's weights, computed with the current m, sum past this bound in some
+// lane (which includes any weight that overflowed).  Below the bound every
+// weight is at most 2^10: well inside fp16 and bf16, and O and l stay exact
+// in fp32.  Random data essentially never comes near it, so the row maximum
+// of a tile is computed only on that rare path.
+constexpr float kTileSumLimit = 1024.0f;
 
 // max / sum of a value over the two halves of the wave (lanes l and l^32):
 // v_permlane32_swap exchanges the halves without going through LDS.
@@ -130,8 +136,6 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
     const size_t head = (size_t)bh * N * D;
     const uint32_t head_bytes = (uint32_t)N * D * 2;
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + head, head_bytes);
     const int q0 = qt * BM;
     const int qw = q0 + wave * 32;    // first query of this wave
     const int my_q = qw + li;
@@ -165,17 +169,29 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
         koff[i] = (uint32_t)(row * D + 8 * (pos ^ swz_k<D>(row))) * 2u;
         voff[i] = (uint32_t)(row * D + 8 * (pos ^ swz_v<D>(row))) * 2u;
     }
+    // The tile's base goes into the (scalar) buffer resource, so the
+    // per-lane offsets stay fixed and the range check still covers the end of
+    // the head: a resource past the end has zero records and reads zeros.
+    auto tile_rsrc = [&](const uint16_t *base, int tile) __attribute__((always_inline)) {
+        const uint32_t off = (uint32_t)tile * (BN * D * 2);
+        const uint64_t addr = (uint64_t)(uintptr_t)base + off;
+        // Uniform values: keep the resource in scalar registers.
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+        const uint32_t n = __builtin_amdgcn_readfirstlane(off < head_bytes ? head_bytes - off : 0u);
+        return make_rsrc((const void *)(uintptr_t)(((uint64_t)hi << 32) | lo), n);
+    };
     auto load_k = [&](int tile, uint16_t *buf) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(k + head, tile);
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
-            buffer_load16_lds(kr, koff[i] + (uint32_t)tile * (BN * D * 2),
-                              buf + (wave * (BN / 4) + i * C::RPI) * D);
+            buffer_load16_lds(r, koff[i], buf + (wave * (BN / 4) + i * C::RPI) * D);
     };
     auto load_v = [&](int tile, uint16_t *buf) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(v + head, tile);
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
-            buffer_load16_lds(vr, voff[i] + (uint32_t)tile * (BN * D * 2),
-                              buf + (wave * (BN / 4) + i * C::RPI) * D);
+            buffer_load16_lds(r, voff[i], buf + (wave * (BN / 4) + i * C::RPI) * D);
     };
 
     // K operand of block kb, step t: logical chunk 2t + lh of row 32kb + li.
@@ -239,21 +255,16 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
             for (int r = kb == 0 ? 2 : 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, x[kb][r]);
         mt = max_halves(mx) * c;
     };
-    // Raise m (and rescale O, l) only when the tile max passes the slack.
+    // m' = max(m, tile max); O and l scaled by 2^(m - m').
     auto raise_max = [&]() __attribute__((always_inline)) {
-        if (__any(mt > m_run + kRescaleSlack)) {
-            // Rare path: keep it a real branch (the compiler would otherwise
-            // turn it into unconditional multiplies of the whole O tile).
-            asm volatile("" ::: "memory");
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        }
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     };
 
     // P^T operands: register r of block kb becomes element r%8 of operand
@@ -261,15 +272,35 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
     // 32kb + 16u + 8(e/4) + 4lh + e%4.
     vec8 pb[KB][2];
     // m is finite from tile 0 on (every query sees key 0), so the softmax
-    // needs no guard against an infinite base.
+    // needs no guard against an infinite base.  tsum collects this lane's
+    // part of the tile's row sum.
+    float tsum = 0.f;
     auto softmax_part = [&](const floatx16 (&x)[KB], int kb, int u) __attribute__((always_inline)) {
+        if (kb == 0 && u == 0) tsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float p = __builtin_amdgcn_exp2f(fmaf(x[kb][8 * u + e], c, -m_run));
-            if constexpr (!T::kSumP) l_run += p;
+            if constexpr (!T::kSumP) tsum += p;
             pb[kb][u][e] = (scalar)p;
         }
-        if constexpr (T::kSumP) l_run = T::sum8(pb[kb][u], l_run);
+        if constexpr (T::kSumP) tsum = T::sum8(pb[kb][u], tsum);
+    };
+    // Accept the tile's weights, or (rare) raise m to the tile's exact
+    // maximum, rescale O and l, and recompute the weights.  The negated test
+    // also catches an infinite sum.
+    auto accept = [&](const floatx16 (&x)[KB]) __attribute__((always_inline)) {
+        if (__any(!(tsum <= kTileSumLimit))) {
+            // Keep this a real branch: the compiler would otherwise turn it
+            // into unconditional work on every tile.
+            asm volatile("" ::: "memory");
+            row_max(x);
+            raise_max();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) softmax_part(x, kb, u);
+        }
+        l_run += tsum;
     };
 
     // Tiles before n_full need no mask for any query of the workgroup: all
@@ -296,13 +327,13 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
     __syncthreads();
 
     // Iteration j (parity PAR = j % 2): softmax of tile j next to QK^T of
-    // tile j+1, then PV of tile j next to the row maximum of tile j+1.  LDS
-    // holds K(j+1) in K[1-PAR] and V(j) in V[PAR]; K(j+2) and V(j+1) are
-    // copied meanwhile into K[PAR] and V[1-PAR], which iteration j-1 finished
-    // reading, and the barrier at the end publishes them.  Two waves share
-    // each SIMD, so one wave's softmax overlaps the other's MFMAs; the order
-    // below additionally gives every wave independent work next to each
-    // MFMA.  Phase boundaries are fenced so the compiler keeps that order.
+    // tile j+1, then PV of tile j.  LDS holds K(j+1) in K[1-PAR] and V(j) in
+    // V[PAR]; K(j+2) and V(j+1) are copied meanwhile into K[PAR] and V[1-PAR],
+    // which iteration j-1 finished reading, and the barrier at the end
+    // publishes them.  Two waves share each SIMD, so one wave's exponentials
+    // run under the other's MFMAs; inside a wave, the exponentials of tile j
+    // are also independent of the QK^T MFMAs next to them.  Phase boundaries
+    // are fenced so the compiler keeps that order.
     auto iteration = [&](int j, auto par, auto mask_tag, floatx16 (&cur)[KB],
                          floatx16 (&nxt)[KB]) __attribute__((always_inline)) {
         constexpr bool MASK_NEXT = decltype(mask_tag)::value;
@@ -314,19 +345,19 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
 
         load_k(j + 2, kb_fill);
         load_v(j + 1, vb_fill);
-        // Phase 1: QK^T(j+1) | softmax(j) of key block 0.
+        // Phase 1: QK^T(j+1) | softmax(j).
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int t = 0; t < KSTEPS; ++t) {
                 nxt[kb] = T::mfma32(read_k(kb_next, kb, t), qf[t], t == 0 ? zero16 : nxt[kb]);
-                if (kb == 0 && t == 1) softmax_part(cur, 0, 0);
-                if (kb == 0 && t == KSTEPS / 2 + 1) softmax_part(cur, 0, 1);
-                if (KB > 1 && kb == 1 && t == 1) softmax_part(cur, KB - 1, 0);
+                if (t == 1) softmax_part(cur, kb, 0);
+                if (t == KSTEPS / 2 + 1) softmax_part(cur, kb, 1);
             }
         __builtin_amdgcn_sched_barrier(0);
-        // Phase 2: PV(j) | rest of softmax(j) | row maximum of tile j+1.
-        if constexpr (KB > 1) softmax_part(cur, KB - 1, 1);
+        accept(cur);
+        __builtin_amdgcn_sched_barrier(0);
+        // Phase 2: PV(j) | mask of tile j+1.
         if constexpr (MASK_NEXT) mask(nxt, j + 1);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -335,9 +366,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
                     oacc[db] = T::mfma32(read_v(vb_cur, kb, u, db), pb[kb][u], oacc[db]);
-        row_max(nxt);
         __builtin_amdgcn_sched_barrier(0);
-        raise_max();
         wait_vmem();
         __syncthreads();
     };
@@ -361,12 +390,15 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                softmax_part(cur, kb, u);
+            for (int u = 0; u < 2; ++u) softmax_part(cur, kb, u);
+        accept(cur);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
                     oacc[db] = T::mfma32(read_v(vb, kb, u, db), pb[kb][u], oacc[db]);
-            }
     };
     if ((ntiles - 1) & 1) last(sB, V1); else last(sA, V0);
 
