@@ -16,8 +16,9 @@
 // of them.  The 4 waves take interleaved 32-key blocks of the shard; each
 // wave keeps its own online-softmax state and the 4 states are merged through
 // LDS at the end.  This kernel is bound by HBM bandwidth: MFMA and VALU work
-// hide under the K/V stream, and the next block's loads are issued before
-// the current block is computed.
+// hide under the K/V stream, the next block's loads are issued before the
+// current block is computed, and the cache is read with non-temporal loads
+// (every byte of it is used once).
 //
 // MFMA 16x16x32 (16 columns = up to 16 query heads of one group):
 //   S^T (16 keys x 16 heads) = K (16 x 32 dims) Q^T, K straight from global
@@ -124,11 +125,11 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
         for (int beta = 0; beta < 2; ++beta)
 #pragma unroll
             for (int t = 0; t < D / 32; ++t)
-                bf.kf[beta][t] = buffer_load16(
+                bf.kf[beta][t] = buffer_load16_stream(
                     kr, (uint32_t)((key0 + 16 * beta + lj) * D + 32 * t + 8 * lg) * 2u);
 #pragma unroll
         for (int r = 0; r < C::VLOADS; ++r)
-            bf.vr[r] = buffer_load16(vr, (uint32_t)((key0 + vrow + C::VROWS * r) * D + 8 * dc) * 2u);
+            bf.vr[r] = buffer_load16_stream(vr, (uint32_t)((key0 + vrow + C::VROWS * r) * D + 8 * dc) * 2u);
     };
 
     floatx4 oacc[D / 16];
