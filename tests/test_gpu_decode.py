@@ -34,6 +34,11 @@ def test_decode_config(orc):
     run(orc, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], c["nsplit"], c["dtype"], c["seed"])
 
 
+def test_long_cache(orc):
+    """A 4M-key cache (1 GiB per KV head and tensor): offsets near 2^30 bytes."""
+    run(orc, 1, 8, 1, 1 << 22, 128, 64, seed=1007)
+
+
 @pytest.mark.parametrize("L,nsplit", [(1, 1), (1, 4), (5, 4), (31, 1), (33, 2), (1000, 7),
                                       (777, 16), (64, 64), (40, 100), (4096, 3), (2049, 16)])
 def test_split_counts(orc, L, nsplit):

@@ -75,6 +75,13 @@ def test_long_causal_sampled(orc):
     run_rows(orc, c, rows)
 
 
+def test_long_single_head_causal(orc):
+    """A 2M-token head: per-head offsets past 2^29 bytes, 32768 key tiles."""
+    c = dict(B=1, H=1, N=1 << 21, d=128, dtype="bf16", causal=True, seed=1006)
+    rows = synth.boundary_rows(1, 1, c["N"], seed=c["seed"], tiles=(64, 128, 256), n_random=8)
+    run_rows(orc, c, rows)
+
+
 # -- several tiles with ragged tails, both dtypes and head dims ---------------------
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
