@@ -26,35 +26,19 @@ constexpr float kLn2 = 0.6931471805599453f;
 // (column = lane%32); lanes 32..63 hold the second half of the 16-wide
 // contraction.  C: lane%32 is the column, register r of lane half h is row
 // 8*(r/4) + 4*h + r%4.
-//
-// sum8(p, l): l + the sum of the 8 rounded weights in p, or nothing (kSumP
-// false) when the row sum must be taken from the fp32 weights instead: a
-// bf16 weight carries up to 2^-9 relative rounding error, too much for the
-// log-sum-exp, while fp16's 2^-11 is not.
 struct BF16 {
     typedef bf16x8 vec8;
     typedef __bf16 scalar;
-    static constexpr bool kSumP = false;
     static __device__ __forceinline__ floatx16 mfma32(vec8 a, vec8 b, floatx16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
-    static __device__ __forceinline__ float sum8(vec8, float l) { return l; }
 };
 
 struct FP16 {
     typedef f16x8 vec8;
     typedef _Float16 scalar;
-    static constexpr bool kSumP = true;
     static __device__ __forceinline__ floatx16 mfma32(vec8 a, vec8 b, floatx16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ float sum8(vec8 p, float l) {
-        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            l = __builtin_amdgcn_fdot2(f16x2{p[2 * i], p[2 * i + 1]}, one, l, false);
-        return l;
     }
 };
 

@@ -273,17 +273,17 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
     vec8 pb[KB][2];
     // m is finite from tile 0 on (every query sees key 0), so the softmax
     // needs no guard against an infinite base.  tsum collects this lane's
-    // part of the tile's row sum.
+    // part of the tile's row sum, from the fp32 weights (the 16-bit rounding
+    // of P, up to 2^-9 relative for bf16, stays out of l and lse).
     float tsum = 0.f;
     auto softmax_part = [&](const floatx16 (&x)[KB], int kb, int u) __attribute__((always_inline)) {
         if (kb == 0 && u == 0) tsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float p = __builtin_amdgcn_exp2f(fmaf(x[kb][8 * u + e], c, -m_run));
-            if constexpr (!T::kSumP) tsum += p;
+            tsum += p;
             pb[kb][u][e] = (scalar)p;
         }
-        if constexpr (T::kSumP) tsum = T::sum8(pb[kb][u], tsum);
     };
     // Accept the tile's weights, or (rare) raise m to the tile's exact
     // maximum, rescale O and l, and recompute the weights.  The negated test
