@@ -6,10 +6,11 @@
 // The running-max / running-sum rescaling is the "online normalisation"
 // the smzdm digest (section 6) tells multi-GPU users to check first.
 //
-// Work split: one workgroup = 4 waves = 128 queries of one (batch, head);
-// each wave owns 32 queries.  Two workgroups share a compute unit, so every
-// SIMD runs two waves (at most 256 registers each): while one wave computes
-// exponentials the other keeps the matrix core busy.  Keys stream through
+// Work split: each wave owns 32 queries of one (batch, head); a workgroup
+// is 8 waves (256 queries) without a mask and 4 waves (128 queries) with the
+// causal mask.  Every SIMD runs two waves (at most 256 registers each):
+// while one wave computes exponentials the other keeps the matrix core
+// busy.  Keys stream through
 // LDS in tiles of 64: the K and V tiles of the coming iterations are copied
 // from global memory straight into the LDS buffers that just became free
 // while the current tile is computed (one barrier per tile).
@@ -43,19 +44,28 @@
 
 namespace fa {
 
-template <int D>
+// Workgroup shape.  Every wave owns 32 queries and every SIMD runs two
+// waves.  Without a mask the workgroup is 8 waves (256 queries, one per CU),
+// so each K/V tile copied into LDS serves twice the queries; with the causal
+// mask it is 4 waves (128 queries, two per CU), which keeps the diagonal
+// tiles that a workgroup must visit, and the tail of the grid, small.
+// Both were picked by measurement on MI355X.
+template <int D, bool CAUSAL>
 struct FwdTile {
-    static constexpr int BM = 128;                // queries per workgroup (32 per wave)
+    static constexpr int WAVES = CAUSAL ? 4 : 8;
+    static constexpr int BM = 32 * WAVES;         // queries per workgroup
     static constexpr int KB = 2;                  // 32-key blocks per tile
     static constexpr int BN = 32 * KB;            // keys per tile
-    static constexpr int THREADS = 256;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int BLOCKS_PER_CU = 8 / WAVES;
     static constexpr int KCH = D / 8;             // 16-byte chunks per row
     static constexpr int RPI = 64 / KCH;          // rows one wave copy instruction covers
-    static constexpr int LOADS = BN / 4 / RPI;    // copy instructions per wave, per tensor, per tile
+    static constexpr int ROWS = BN / WAVES;       // rows of a tile each wave copies
+    static constexpr int LOADS = ROWS / RPI;      // copy instructions per wave, per tensor, per tile
     static constexpr int ELEMS = BN * D;
     // Rows that share a bank line: 64 banks hold 16 chunks, i.e. 16/KCH rows.
     static constexpr int ROWS_PER_LINE = 16 / KCH;
-    static_assert(BN % (4 * RPI) == 0, "tile must split evenly over the waves");
+    static_assert(ROWS % RPI == 0, "tile must split evenly over the waves");
 };
 
 // LDS tiles are unpadded (direct copies write 1 KB contiguous per wave
@@ -69,13 +79,13 @@ struct FwdTile {
 //    disjoint chunk quadruples.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
-    typedef FwdTile<D> C;
-    return (r / C::ROWS_PER_LINE) % C::KCH;
+    constexpr int KCH = D / 8, ROWS_PER_LINE = 16 / KCH;
+    return (r / ROWS_PER_LINE) % KCH;
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
-    typedef FwdTile<D> C;
-    return 4 * ((r / C::ROWS_PER_LINE) % (C::KCH / 4));
+    constexpr int KCH = D / 8, ROWS_PER_LINE = 16 / KCH;
+    return 4 * ((r / ROWS_PER_LINE) % (KCH / 4));
 }
 
 // Bound on one lane's sum of the unnormalised weights of a tile.  The running
@@ -101,11 +111,13 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
+__global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, float *__restrict__ o,
     float *__restrict__ lse, int N, int nq, float c, uint32_t qand, uint32_t qxor) {
-    typedef FwdTile<D> C;
+    typedef FwdTile<D, CAUSAL> C;
+    static_assert(C::THREADS == (CAUSAL ? 256 : 512) && C::BLOCKS_PER_CU == (CAUSAL ? 2 : 1),
+                  "launch bounds must match the tile shape");
     typedef typename T::vec8 vec8;
     typedef typename T::scalar scalar;
     constexpr int BM = C::BM, BN = C::BN, KB = C::KB, KCH = C::KCH;
@@ -156,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
     const int ntiles = (kv_end + BN - 1) / BN;
 
     // Tile copies go straight from global memory into LDS.  Wave w copies
-    // rows [w*BN/4, (w+1)*BN/4) of a tile, RPI rows per instruction; lane l
+    // rows [w*ROWS, (w+1)*ROWS) of a tile, RPI rows per instruction; lane l
     // fills chunk position l%KCH of its row with the source chunk that the
     // swizzle puts there.  Rows past N read as zero (buffer range check) and
     // are masked out of the softmax; tiles past the last one are copied the
@@ -164,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
     uint32_t koff[C::LOADS], voff[C::LOADS];
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-        const int row = wave * (BN / 4) + i * C::RPI + lane / KCH;
+        const int row = wave * C::ROWS + i * C::RPI + lane / KCH;
         const int pos = lane % KCH;
         koff[i] = (uint32_t)(row * D + 8 * (pos ^ swz_k<D>(row))) * 2u;
         voff[i] = (uint32_t)(row * D + 8 * (pos ^ swz_v<D>(row))) * 2u;
@@ -185,13 +197,13 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
         const __amdgpu_buffer_rsrc_t r = tile_rsrc(k + head, tile);
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
-            buffer_load16_lds(r, koff[i], buf + (wave * (BN / 4) + i * C::RPI) * D);
+            buffer_load16_lds(r, koff[i], buf + (wave * C::ROWS + i * C::RPI) * D);
     };
     auto load_v = [&](int tile, uint16_t *buf) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t r = tile_rsrc(v + head, tile);
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
-            buffer_load16_lds(r, voff[i], buf + (wave * (BN / 4) + i * C::RPI) * D);
+            buffer_load16_lds(r, voff[i], buf + (wave * C::ROWS + i * C::RPI) * D);
     };
 
     // K operand of block kb, step t: logical chunk 2t + lh of row 32kb + li.
@@ -422,7 +434,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch(const FwdArgs &a, hipStream_t stream) {
-    typedef FwdTile<D> C;
+    typedef FwdTile<D, CAUSAL> C;
     const int nq = (a.N + C::BM - 1) / C::BM;
     const long long blocks = (long long)nq * a.BH;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
