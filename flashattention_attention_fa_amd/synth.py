@@ -49,6 +49,27 @@ def fwd_inputs(B, H, N, d, dtype="bf16", seed=0, device="cpu",
     return q, k, v
 
 
+def fp8_inputs(B, H, N, d, seed=0, device="cpu", amp=8.0):
+    """FP8 (E4M3) q, k, v of shape [B, H, N, d] as uint8 tensors holding the
+    E4M3 bytes, and their per-tensor dequantization factor 1/amp: each
+    tensor is amp * N(0, 1) drawn in fp32 (seeds as fwd_inputs) and rounded
+    to E4M3 (nearest even), so the dequantized values follow N(0, 1)."""
+    base = int(seed) * 16
+    out = []
+    for i in range(3):
+        g = torch.Generator(device=device).manual_seed(base + i)
+        x = torch.randn((B, H, N, d), generator=g, device=device, dtype=torch.float32)
+        out.append((x * amp).to(torch.float8_e4m3fn).view(torch.uint8))
+    return out[0], out[1], out[2], 1.0 / amp
+
+
+def fp8_bits(t: torch.Tensor) -> np.ndarray:
+    """uint8 E4M3 tensor -> host numpy uint8 (what the oracle reads)."""
+    if t.dtype != torch.uint8:
+        raise TypeError("expected a uint8 tensor of E4M3 bytes")
+    return t.detach().contiguous().cpu().numpy()
+
+
 def decode_inputs(B, Hq, Hkv, L, d, dtype="bf16", seed=0, device="cpu"):
     """q [B, Hq, d] (one new token per sequence), kcache/vcache [B, Hkv, L, d]."""
     base = int(seed) * 16

@@ -20,6 +20,10 @@
  *  - Same page, "Benchmarking Triton vs FlashAttention-3 Kernels": tensors
  *    are laid out (batch, heads, seq_len, head_dim) and the benchmarked call
  *    is the non-causal default, whose scale is 1/sqrt(head_dim).
+ *  - Same page, introduction and the pipeline figure: the FP8 variant of the
+ *    forward.  Its oracle is the same definition on the dequantized inputs
+ *    dq*q8, dk*k8, dv*v8 (per-tensor factors), with E4M3 bytes widened
+ *    exactly (oracle_attention_rows_dq, dtype ORACLE_FP8).
  *  - post.smzdm.com digest on Triton warp specialisation, section 5
  *    (attention cannot be split like a GEMM): partial attention outputs over
  *    disjoint key shards cannot be added, because each shard has its own
@@ -33,8 +37,8 @@
  * lse is the natural log; a query with no visible key gets O = 0 and
  * lse = -inf.
  *
- * Precision: inputs are the exact 16-bit values the GPU consumes (bf16 or
- * fp16 bit patterns), widened exactly to double; everything after that is
+ * Precision: inputs are the exact values the GPU consumes (bf16, fp16 or
+ * E4M3 bit patterns), widened exactly to double; everything after that is
  * plain fp64 in a two-pass (max, then exp-sum) softmax.
  *
  * ORACLE_MUTANT (compile-time, default 0) plants one deliberate mistake per
@@ -52,10 +56,29 @@
 
 #define ORACLE_BF16 0
 #define ORACLE_FP16 1
+#define ORACLE_FP8 2    /* OCP E4M3 ("e4m3fn"), one byte per element */
 
 /* Exact widening of one 16-bit storage value to double. */
 double oracle_widen(uint16_t bits, int dtype)
 {
+    if (dtype == ORACLE_FP8) {
+        /* E4M3: 1 sign, 4 exponent (bias 7), 3 fraction bits; exponent 15
+         * with fraction 7 is NaN; there are no infinities. */
+        int sign8 = (bits >> 7) & 1, e8 = (bits >> 3) & 15, f8 = bits & 7;
+#if ORACLE_MUTANT == 13
+        const int bias8 = 8;
+#else
+        const int bias8 = 7;
+#endif
+        double mag8;
+        if (e8 == 15 && f8 == 7)
+            mag8 = NAN;
+        else if (e8 == 0)
+            mag8 = ldexp((double)f8, 1 - bias8 - 3);         /* subnormal */
+        else
+            mag8 = ldexp((double)(8 + f8), e8 - bias8 - 3);
+        return sign8 ? -mag8 : mag8;
+    }
     if (dtype == ORACLE_BF16) {
         /* bfloat16 is the top half of an IEEE binary32. */
 #if ORACLE_MUTANT == 11
@@ -110,20 +133,23 @@ static int key_visible(long j, long i, int causal)
 
 /*
  * Attention for an explicit list of query rows, restricted to keys in
- * [klo, khi) (the full key set is [0, Nk)).
+ * [klo, khi) (the full key set is [0, Nk)), on the dequantized inputs
+ * dq*q, dk*k, dv*v (dq = dk = dv = 1 for 16-bit inputs).
  *
- *   q     [B, Hq,  Nq, d]  16-bit bit patterns, d fastest
- *   k, v  [B, Hkv, Nk, d]  16-bit bit patterns
+ *   q     [B, Hq,  Nq, d]  bit patterns, d fastest (FP8 bytes zero-extended
+ *                          to 16 bits)
+ *   k, v  [B, Hkv, Nk, d]  bit patterns
  *   rows  nrows triples (b, hq, i)
  *   out_o [nrows, d] double, out_lse [nrows] double
  *
  * Returns 0, or -1 on a bad argument (nothing written).
  */
-int oracle_attention_rows(const uint16_t *q, const uint16_t *k,
-                          const uint16_t *v, int dtype, long B, long Hq,
-                          long Hkv, long Nq, long Nk, long d, int causal,
-                          double scale, long klo, long khi, const long *rows,
-                          long nrows, double *out_o, double *out_lse)
+int oracle_attention_rows_dq(const uint16_t *q, const uint16_t *k,
+                             const uint16_t *v, int dtype, double dq, double dk,
+                             double dv, long B, long Hq, long Hkv, long Nq,
+                             long Nk, long d, int causal, double scale, long klo,
+                             long khi, const long *rows, long nrows,
+                             double *out_o, double *out_lse)
 {
     if (!q || !k || !v || !rows || !out_o || !out_lse)
         return -1;
@@ -160,7 +186,7 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k,
 #endif
             double *o = out_o + r * d;
             for (long c = 0; c < d; ++c)
-                qd[c] = oracle_widen(qi[c], dtype);
+                qd[c] = dq * oracle_widen(qi[c], dtype);
 
             /* pass 1: scores of the visible keys and their maximum */
             double m = -INFINITY;
@@ -175,7 +201,7 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k,
 #else
                 for (long c = 0; c < d; ++c)
 #endif
-                    dot += qd[c] * oracle_widen(kj[c], dtype);
+                    dot += qd[c] * (dk * oracle_widen(kj[c], dtype));
 #if ORACLE_MUTANT == 1
                 s[j] = -scale * dot;
 #else
@@ -204,8 +230,13 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k,
 #else
                 const uint16_t *vj = vb + j * d;
 #endif
+#if ORACLE_MUTANT == 14
                 for (long c = 0; c < d; ++c)
                     o[c] += p * oracle_widen(vj[c], dtype);
+#else
+                for (long c = 0; c < d; ++c)
+                    o[c] += p * (dv * oracle_widen(vj[c], dtype));
+#endif
             }
 #if ORACLE_MUTANT != 6
             for (long c = 0; c < d; ++c)
@@ -221,6 +252,18 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k,
         free(qd);
     }
     return bad ? -1 : 0;
+}
+
+/* The same for undequantized (16-bit) inputs. */
+int oracle_attention_rows(const uint16_t *q, const uint16_t *k,
+                          const uint16_t *v, int dtype, long B, long Hq,
+                          long Hkv, long Nq, long Nk, long d, int causal,
+                          double scale, long klo, long khi, const long *rows,
+                          long nrows, double *out_o, double *out_lse)
+{
+    return oracle_attention_rows_dq(q, k, v, dtype, 1.0, 1.0, 1.0, B, Hq, Hkv,
+                                    Nq, Nk, d, causal, scale, klo, khi, rows,
+                                    nrows, out_o, out_lse);
 }
 
 /*

@@ -7,8 +7,9 @@ imports this module, and this module imports nothing from the product.
 The arithmetic lives in ``fa_oracle.c`` (plain C, fp64, OpenMP over rows);
 this file builds it with gcc and marshals numpy arrays through ctypes.
 
-Inputs are 16-bit bit patterns (``numpy.uint16``) of bf16 or fp16 values,
-exactly the values a GPU kernel would consume; the C code widens them to
+Inputs are bit patterns of the values a GPU kernel would consume: 16-bit
+(``numpy.uint16``) bf16 or fp16, or bytes (``numpy.uint8``) of FP8 E4M3 with
+per-tensor dequantization factors; the C code widens them exactly to
 double.  Layouts follow the (batch, heads, seq_len, head_dim) convention of
 the benchmark listing on the dailyaiworld page "FlashAttention-3 vs Triton
 Kernels", section "Benchmarking Triton vs FlashAttention-3 Kernels".
@@ -26,7 +27,7 @@ _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "fa_oracle.c"
 _LIB_PATH = _HERE / "libfa_oracle.so"
 
-DTYPES = {"bf16": 0, "fp16": 1}
+DTYPES = {"bf16": 0, "fp16": 1, "fp8": 2}
 
 
 def build(out: Path | None = None, mutant: int = 0) -> Path:
@@ -56,6 +57,9 @@ class Oracle:
         self.lib.oracle_attention_rows.argtypes = [P, P, P, I, L, L, L, L, L, L,
                                                    I, D, L, L, P, L, P, P]
         self.lib.oracle_attention_rows.restype = I
+        self.lib.oracle_attention_rows_dq.argtypes = [P, P, P, I, D, D, D, L, L, L, L, L,
+                                                      L, I, D, L, L, P, L, P, P]
+        self.lib.oracle_attention_rows_dq.restype = I
         self.lib.oracle_combine.argtypes = [P, P, L, L, P, P]
         self.lib.oracle_combine.restype = None
         self.lib.oracle_decode.argtypes = [P, P, P, I, L, L, L, L, L, P, P]
@@ -100,6 +104,42 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_attention_rows rejected its arguments")
         return o, lse
+
+    def attention_rows_fp8(self, q, k, v, rows, causal: bool, scale: float,
+                           dq: float, dk: float, dv: float):
+        """FP8 E4M3 inputs (uint8 bytes) with dequantization factors: the
+        attention of dq*q, dk*k, dv*v over explicit rows."""
+        arrs = []
+        for a in (q, k, v):
+            a = np.ascontiguousarray(a)
+            if a.dtype != np.uint8:
+                raise TypeError("FP8 oracle inputs are uint8 bytes")
+            arrs.append(a.astype(np.uint16))
+        q, k, v = arrs
+        B, Hq, Nq, d = q.shape
+        Bk, Hkv, Nk, dk_ = k.shape
+        if v.shape != k.shape or Bk != B or dk_ != d:
+            raise ValueError("shape mismatch")
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+        n = rows.shape[0]
+        o = np.zeros((n, d), np.float64)
+        lse = np.zeros(n, np.float64)
+        rc = self.lib.oracle_attention_rows_dq(
+            self._ptr(q), self._ptr(k), self._ptr(v), DTYPES["fp8"], float(dq), float(dk),
+            float(dv), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(scale), 0, Nk,
+            self._ptr(rows), n, self._ptr(o), self._ptr(lse))
+        if rc != 0:
+            raise ValueError("oracle_attention_rows_dq rejected its arguments")
+        return o, lse
+
+    def attention_fp8(self, q, k, v, causal: bool, scale: float, dq: float, dk: float,
+                      dv: float):
+        """Every row of a [B,H,N,d] FP8 problem."""
+        B, H, N, d = q.shape
+        bb, hh, ii = np.meshgrid(np.arange(B), np.arange(H), np.arange(N), indexing="ij")
+        rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
+        o, lse = self.attention_rows_fp8(q, k, v, rows, causal, scale, dq, dk, dv)
+        return o.reshape(B, H, N, d), lse.reshape(B, H, N)
 
     def attention(self, q, k, v, dtype: str, causal: bool, scale: float):
         """Every row of a [B,H,N,d] problem: (o [B,H,N,d], lse [B,H,N])."""

@@ -267,9 +267,57 @@ def pin_decode_gqa(orc):
     np.testing.assert_allclose(lse, rl[:, :, 0], rtol=1e-12, atol=1e-12)
 
 
+def fp8_widened(b):
+    """Library widening of E4M3 bytes (torch float8_e4m3fn), for expected values."""
+    t = torch.from_numpy(np.ascontiguousarray(b, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def pin_widen_fp8(orc):
+    """All 256 E4M3 byte patterns widen to torch's float8_e4m3fn values."""
+    bits = np.arange(256, dtype=np.uint8)
+    ref = fp8_widened(bits)
+    for b in bits:
+        got = orc.widen(int(b), "fp8")
+        if math.isnan(ref[b]):
+            assert math.isnan(got), hex(b)
+        else:
+            assert got == ref[b], (hex(b), got, ref[b])
+
+
+def pin_fp8_library_routine(orc):
+    """FP8 attention = torch fp64 SDPA and logsumexp on the dequantized
+    tensors dq*q8, dk*k8, dv*v8 (factors other than 1)."""
+    for causal, shape in ((False, (1, 2, 40, 64)), (True, (1, 2, 50, 32))):
+        q8, k8, v8, _ = synth.fp8_inputs(*shape, seed=22)
+        qb, kb, vb = synth.fp8_bits(q8), synth.fp8_bits(k8), synth.fp8_bits(v8)
+        dq, dk, dv, scale = 0.25, 0.5, 3.0, 1 / math.sqrt(shape[-1])
+        o, lse = orc.attention_fp8(qb, kb, vb, causal, scale, dq, dk, dv)
+        q = torch.from_numpy(dq * fp8_widened(qb))
+        k = torch.from_numpy(dk * fp8_widened(kb))
+        v = torch.from_numpy(dv * fp8_widened(vb))
+        ro = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal, scale=scale)
+        s = scale * (q @ k.transpose(-1, -2).contiguous())
+        if causal:
+            s = s.masked_fill(torch.ones(s.shape[-2:], dtype=torch.bool).triu(1), float("-inf"))
+        np.testing.assert_allclose(o, ro.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def pin_fp8_single_key(orc):
+    """One key: O = dv * v8[0] and lse = scale * dq * dk * <q8, k8[0]>."""
+    q8, k8, v8, _ = synth.fp8_inputs(1, 2, 1, 16, seed=23)
+    qb, kb, vb = synth.fp8_bits(q8), synth.fp8_bits(k8), synth.fp8_bits(v8)
+    o, lse = orc.attention_fp8(qb, kb, vb, False, 0.3, 0.5, 0.25, 2.0)
+    np.testing.assert_allclose(o, 2.0 * fp8_widened(vb), rtol=1e-15)
+    want = 0.3 * 0.5 * 0.25 * (fp8_widened(qb) * fp8_widened(kb)).sum(-1)
+    np.testing.assert_allclose(lse, want, rtol=1e-13)
+
+
 PINS = [pin_widen_all_patterns, pin_worked_examples, pin_single_key, pin_causal_row0,
         pin_uniform_when_q_zero, pin_constant_v, pin_weights_sum_to_one, pin_split_combine,
-        pin_permutation_invariance, pin_library_routine, pin_brute_force, pin_decode_gqa]
+        pin_permutation_invariance, pin_library_routine, pin_brute_force, pin_decode_gqa,
+        pin_widen_fp8, pin_fp8_library_routine, pin_fp8_single_key]
 
 
 @pytest.fixture(scope="module")
@@ -313,6 +361,8 @@ MUTANTS = {
     10: "dot product drops the last head_dim term",
     11: "bf16 widening shifts by 15",
     12: "combine lse drops log of the weight sum",
+    13: "E4M3 exponent bias 8",
+    14: "value dequantization factor dropped",
 }
 
 
