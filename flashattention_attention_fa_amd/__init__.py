@@ -17,7 +17,7 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["fwd", "decode", "decode_workspace_bytes", "lib", "FAError", "LIB_PATH",
+__all__ = ["fwd", "fwd_fp8", "decode", "decode_workspace_bytes", "lib", "FAError", "LIB_PATH",
            "HEADER_PATH", "status_string"]
 
 LIB_PATH = Path(__file__).resolve().parent / "libfa_amd.so"
@@ -42,6 +42,8 @@ def lib() -> ctypes.CDLL:
         P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P, I]
         L.fa_fwd.restype = I
+        L.fa_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, F, F, F, F, P]
+        L.fa_fwd_fp8.restype = I
         L.fa_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, P, I]
         L.fa_decode.restype = I
         L.fa_decode_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, I, P, S]
@@ -63,7 +65,7 @@ def status_string(status: int) -> str:
 def declared_functions() -> list[str]:
     """Names of the functions include/fa.h declares."""
     text = re.sub(r"/\*.*?\*/", "", HEADER_PATH.read_text(), flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(fa_[a-z_]+)\s*\(",
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(fa_[a-z0-9_]+)\s*\(",
                       text, flags=re.M)
 
 
@@ -109,6 +111,37 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
     st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                       int(bool(causal)), float(scale), _stream(stream, q.device), _DTYPE[q.dtype])
     _check(st, "fa_fwd")
+    return out, lse
+
+
+def fwd_fp8(q, k, v, *, q_descale: float, k_descale: float, v_descale: float,
+            causal: bool = False, scale: float | None = None, out=None, lse=None,
+            return_lse: bool = True, stream=None):
+    """Attention forward on FP8 E4M3 inputs: q, k, v are [B, H, N, d] CUDA
+    tensors of E4M3 bytes (torch.uint8, or torch.float8_e4m3fn); the result
+    is the attention of q_descale*q, k_descale*k, v_descale*v.
+    Returns (o [B, H, N, d] fp32, lse [B, H, N] fp32 or None)."""
+    _need(q.dim() == 4 and q.shape == k.shape == v.shape, "q, k, v must share a [B,H,N,d] shape")
+    _need(all(t.dtype in (torch.uint8, torch.float8_e4m3fn) for t in (q, k, v)),
+          "q, k, v must hold E4M3 bytes (uint8 or float8_e4m3fn)")
+    _need(q.is_cuda and k.device == q.device and v.device == q.device, "tensors must be on one GPU")
+    _need(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "tensors must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    _need(out.shape == q.shape and out.dtype == torch.float32 and out.is_contiguous()
+          and out.device == q.device, "out must be a contiguous fp32 [B,H,N,d] tensor")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse.shape == (B, H, N) and lse.dtype == torch.float32 and lse.is_contiguous()
+              and lse.device == q.device, "lse must be a contiguous fp32 [B,H,N] tensor")
+    st = lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                          int(bool(causal)), float(scale), float(q_descale), float(k_descale),
+                          float(v_descale), _stream(stream, q.device))
+    _check(st, "fa_fwd_fp8")
     return out, lse
 
 

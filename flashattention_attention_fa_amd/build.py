@@ -16,12 +16,13 @@ LIB = PKG / "libfa_amd.so"
 BUILD_DIR = ROOT / "_build"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_decode.hip"]
 # Per-source extra flags.  The forward kernel keeps its MFMA accumulators in
 # vector registers (the softmax reads S directly, O stays put); without this
 # the compiler parks them in accumulation registers and copies them back and
 # forth every iteration.
-SOURCE_FLAGS = {"fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "fa_fwd_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 # Packed fp32 VALU instructions are switched off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

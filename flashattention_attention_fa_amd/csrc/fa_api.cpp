@@ -121,6 +121,42 @@ fa_status_t fa_fwd(const void *q, const void *k, const void *v, float *o, float 
     }
 }
 
+fa_status_t fa_fwd_fp8(const void *q, const void *k, const void *v, float *o, float *lse,
+                       int B, int H, int N, int d, int causal, float scale, float q_descale,
+                       float k_descale, float v_descale, hipStream_t stream) {
+    try {
+        if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
+        if (!std::isfinite(scale) || !std::isfinite(q_descale) || !std::isfinite(k_descale) ||
+            !std::isfinite(v_descale))
+            return FA_ERR_VALUE;
+        if (B == 0 || H == 0 || N == 0) return FA_OK;
+        if (!q || !k || !v || !o) return FA_ERR_NULL;
+        if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+            (lse && !aligned(lse, 4)))
+            return FA_ERR_ALIGN;
+        const long long BH = (long long)B * H;
+        if (N > kMaxSeq || BH > INT_MAX || BH * ((N + 127) / 128) > INT_MAX) return FA_ERR_SHAPE;
+        fa::FwdFp8Args a;
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.o = o;
+        a.lse = lse;
+        a.BH = (int)BH;
+        a.N = N;
+        a.d = d;
+        a.causal = causal != 0;
+        a.scale = scale;
+        a.qd = q_descale;
+        a.kd = k_descale;
+        a.vd = v_descale;
+        return fa::launch_fwd_fp8(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    } catch (...) {
+        return FA_ERR_INTERNAL;
+    }
+}
+
 size_t fa_decode_workspace_bytes(int B, int Hq, int d, int nsplit) {
     size_t o_bytes = 0, total = 0;
     if (d != 64 && d != 128) return 0;
@@ -192,11 +228,11 @@ const char *fa_status_string(fa_status_t status) {
         case FA_ERR_WORKSPACE: return "decode workspace missing, misaligned or too small";
         case FA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
         case FA_ERR_INTERNAL: return "internal error";
-        case FA_ERR_VALUE: return "scale is not finite";
+        case FA_ERR_VALUE: return "scale or a dequantization factor is not finite";
     }
     return "unknown status";
 }
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 200; }
 
 }  // extern "C"

@@ -100,6 +100,19 @@ __device__ __forceinline__ V join8(shortx4 lo, shortx4 hi) {
     return __builtin_bit_cast(V, x);
 }
 
+// max / sum of a value over the two halves of the wave (lanes l and l^32):
+// v_permlane32_swap exchanges the halves without going through LDS.
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Workgroups are handed to the 8 XCDs round-robin (hardware id % 8).  Remap
 // so that consecutive logical ids run on the same XCD and share its L2:
 // hardware ids x, x+8, x+16, ... become one contiguous logical range.

@@ -97,19 +97,6 @@ __device__ __forceinline__ int swz_v(int r) {
 // of a tile is computed only on that rare path.
 constexpr float kTileSumLimit = 1024.0f;
 
-// max / sum of a value over the two halves of the wave (lanes l and l^32):
-// v_permlane32_swap exchanges the halves without going through LDS.
-__device__ __forceinline__ float max_halves(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                    false, false);
-    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_halves(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                    false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,

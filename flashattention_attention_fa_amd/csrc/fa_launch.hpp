@@ -19,6 +19,18 @@ struct FwdArgs {
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 
+// FP8 (E4M3) forward: q, k, v are [BH, N, d] bytes; the attention is that of
+// the dequantized tensors qd*q, kd*k, vd*v.
+struct FwdFp8Args {
+    const void *q, *k, *v;
+    float *o, *lse;
+    int BH, N, d;
+    bool causal;
+    float scale, qd, kd, vd;
+};
+
+hipError_t launch_fwd_fp8(const FwdFp8Args &a, hipStream_t stream);
+
 struct DecodeArgs {
     const void *q;          // [B, Hq, d] 16-bit
     const void *k, *v;      // [B, Hkv, L, d] 16-bit

@@ -62,6 +62,31 @@ fa_status_t fa_fwd(const void *q, const void *k, const void *v, float *o,
                    float scale, hipStream_t stream, fa_dtype_t dtype);
 
 /*
+ * fa_fwd_fp8 -- fa_fwd for FP8 inputs with per-tensor dequantization
+ * factors: the FP8 variant of the tiled forward that the dailyaiworld page
+ * features (introduction and pipeline figure).  q, k, v hold OCP E4M3
+ * ("e4m3fn": 1 sign, 4 exponent bits with bias 7, 3 fraction bits, largest
+ * finite 448, no infinities) bytes; the result is fa_fwd's definition
+ * applied to the dequantized tensors
+ *     q = q_descale * q8,   k = k_descale * k8,   v = v_descale * v8
+ * (same mask, lse and output layout).  Both products run in E4M3 with fp32
+ * accumulation: the attention weights are rounded to E4M3 for the PV product
+ * (relative error up to 2^-4 per weight), while the row sums and lse use the
+ * fp32 weights.
+ *
+ *   q, k, v : [B, H, N, d] bytes, device, 16-byte aligned
+ *   o, lse  : as fa_fwd (lse may be NULL)
+ *   d       : 64 or 128;  N <= 2^23
+ *   scale, q_descale, k_descale, v_descale : finite (else FA_ERR_VALUE)
+ * Bytes holding the E4M3 NaN pattern (0x7f, 0xff) give undefined results.
+ * B == 0, H == 0 or N == 0 is a no-op returning FA_OK.
+ */
+fa_status_t fa_fwd_fp8(const void *q, const void *k, const void *v, float *o,
+                       float *lse, int B, int H, int N, int d, int causal,
+                       float scale, float q_descale, float k_descale,
+                       float v_descale, hipStream_t stream);
+
+/*
  * fa_decode -- attention of one new query token per sequence against a
  * key/value cache, split along the cache length into nsplit shards whose
  * partial results (O_s, lse_s) are combined by log-sum-exp reweighting

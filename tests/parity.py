@@ -23,12 +23,13 @@ def report(o, ro, lse=None, rl=None):
     return out
 
 
-def assert_close(o, ro, lse=None, rl=None, what=""):
+def assert_close(o, ro, lse=None, rl=None, what="", o_max_abs=O_MAX_ABS, o_rel_l2=O_REL_L2,
+                 lse_max_abs=LSE_MAX_ABS):
     assert np.isfinite(np.asarray(o)).all(), f"{what}: non-finite output"
     r = report(o, ro, lse, rl)
     print(f"{what}: {r}", flush=True)
-    assert r["max_abs"] <= O_MAX_ABS, (what, r)
-    assert r["rel_l2"] <= O_REL_L2, (what, r)
+    assert r["max_abs"] <= o_max_abs, (what, r)
+    assert r["rel_l2"] <= o_rel_l2, (what, r)
     if lse is not None:
-        assert r["lse_max_abs"] <= LSE_MAX_ABS, (what, r)
+        assert r["lse_max_abs"] <= lse_max_abs, (what, r)
     return r

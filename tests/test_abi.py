@@ -19,7 +19,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = fa.declared_functions()
-    assert set(names) >= {"fa_fwd", "fa_decode", "fa_decode_ex", "fa_decode_workspace_bytes",
+    assert set(names) >= {"fa_fwd", "fa_fwd_fp8", "fa_decode", "fa_decode_ex", "fa_decode_workspace_bytes",
                           "fa_status_string", "fa_version"}
     for n in names:
         assert hasattr(L, n), n
@@ -51,6 +51,26 @@ def test_fwd_validation(L):
     assert fwd(L, scale=float("inf")) == VALUE
     assert fwd(L, N=(1 << 23) + 1) == SHAPE
     assert fwd(L, B=65536, H=65536) == SHAPE
+
+
+def fwd8(L, q=A, k=A, v=A, o=A, lse=None, B=1, H=1, N=16, d=64, causal=0, scale=0.125,
+         dq=1.0, dk=1.0, dv=1.0):
+    return L.fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, dq, dk, dv, None)
+
+
+def test_fwd_fp8_validation(L):
+    assert fwd8(L, q=None) == NULL
+    assert fwd8(L, v=None) == NULL
+    assert fwd8(L, B=-1) == SHAPE
+    assert fwd8(L, d=32) == UNSUP
+    assert fwd8(L, q=MIS) == ALIGN
+    assert fwd8(L, lse=A + 1) == ALIGN
+    assert fwd8(L, scale=float("nan")) == VALUE
+    assert fwd8(L, dq=float("inf")) == VALUE
+    assert fwd8(L, dk=float("nan")) == VALUE
+    assert fwd8(L, dv=float("-inf")) == VALUE
+    assert fwd8(L, N=(1 << 23) + 1) == SHAPE
+    assert fwd8(L, q=None, k=None, v=None, o=None, B=0) == OK
 
 
 def test_fwd_empty_is_noop(L):

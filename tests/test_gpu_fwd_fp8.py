@@ -1,0 +1,132 @@
+"""fa_fwd_fp8 through the C ABI on an MI355X, against the fp64 oracle on the
+dequantized inputs.
+
+Tolerance, derived from the arithmetic: the kernel rounds each attention
+weight to E4M3 for the PV product (3 fraction bits: relative error at most
+2^-4, about 2^-4/sqrt(3) = 3.6e-2 RMS for round-to-nearest), while the row
+sum and lse use the fp32 weights.  The output error is then a weighted sum of
+independent per-weight errors, so its RMS relative to O is about 3.6e-2 when
+the weights are spread out and less when one weight dominates; the bar is
+O rel-L2 <= 6e-2 over the checked set.  The element-wise bound is 2^-4 times
+the largest |v| that contributes; with dequantized N(0,1) values (|v| < 6)
+O max-abs <= 0.2.  Scores are exact products of E4M3 values accumulated in
+fp32, so lse keeps the 16-bit bar of 1e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import flashattention_attention_fa_amd as fa
+from flashattention_attention_fa_amd import synth
+from oracle import oracle as oracle_mod
+from parity import assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+FP8_O_MAX_ABS = 0.2
+FP8_O_REL_L2 = 6e-2
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle_mod.get()
+
+
+def check(o, ro, lse, rl, what):
+    return assert_close(o, ro, lse, rl, what, o_max_abs=FP8_O_MAX_ABS, o_rel_l2=FP8_O_REL_L2)
+
+
+def run_full(orc, B, H, N, d, causal, seed, scale=None, dq_mul=1.0):
+    print(f"case fwd_fp8 B{B} H{H} N{N} d{d} causal={causal} seed={seed}", flush=True)
+    q, k, v, ds = synth.fp8_inputs(B, H, N, d, seed=seed, device=DEV)
+    scale = 1 / math.sqrt(d) if scale is None else scale
+    dq, dk, dv = ds * dq_mul, ds, ds
+    o, lse = fa.fwd_fp8(q, k, v, q_descale=dq, k_descale=dk, v_descale=dv, causal=causal,
+                        scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = orc.attention_fp8(synth.fp8_bits(q), synth.fp8_bits(k), synth.fp8_bits(v), causal,
+                               scale, dq, dk, dv)
+    return check(o.cpu().numpy(), ro, lse.cpu().numpy(), rl,
+                 f"fwd_fp8 B{B} H{H} N{N} d{d} causal={causal}")
+
+
+def run_rows(orc, B, H, N, d, causal, seed, rows):
+    print(f"case fwd_fp8 B{B} H{H} N{N} d{d} causal={causal} seed={seed} rows={len(rows)}", flush=True)
+    q, k, v, ds = synth.fp8_inputs(B, H, N, d, seed=seed, device=DEV)
+    scale = 1 / math.sqrt(d)
+    o, lse = fa.fwd_fp8(q, k, v, q_descale=ds, k_descale=ds, v_descale=ds, causal=causal,
+                        scale=scale)
+    torch.cuda.synchronize()
+    r = torch.as_tensor(rows)
+    og = o[r[:, 0], r[:, 1], r[:, 2]].cpu().numpy()
+    lg = lse[r[:, 0], r[:, 1], r[:, 2]].cpu().numpy()
+    del o, lse
+    qb, kb, vb = synth.fp8_bits(q), synth.fp8_bits(k), synth.fp8_bits(v)
+    del q, k, v
+    torch.cuda.empty_cache()
+    ro, rl = orc.attention_rows_fp8(qb, kb, vb, rows, causal, scale, ds, ds, ds)
+    return check(og, ro, lg, rl, f"fwd_fp8 sampled {len(rows)} rows")
+
+
+def test_tiny(orc):
+    run_full(orc, 1, 2, 128, 64, False, seed=2001)
+    run_full(orc, 1, 2, 128, 64, True, seed=2001)
+
+
+def test_bench_shape_sampled(orc):
+    rows = synth.sample_rows(8, 32, 8192, 256, seed=2002)
+    run_rows(orc, 8, 32, 8192, 128, False, 2002, rows)
+
+
+def test_causal_sampled(orc):
+    rows = synth.boundary_rows(4, 32, 16384, seed=2003, n_random=96)
+    run_rows(orc, 4, 32, 16384, 128, True, 2003, rows)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_multi_tile(orc, causal, d):
+    run_full(orc, 2, 3, 333, d, causal, seed=2010 + d)
+
+
+@pytest.mark.parametrize("N", [1, 2, 31, 63, 64, 65, 127, 129, 257])
+def test_lengths(orc, N):
+    run_full(orc, 1, 2, N, 128, N % 2 == 1, seed=N)
+
+
+def test_scale_and_descale_signs(orc):
+    run_full(orc, 1, 2, 150, 128, True, seed=2020, scale=-0.2)
+    run_full(orc, 1, 2, 150, 128, False, seed=2021, scale=0.0)
+    run_full(orc, 1, 2, 150, 64, True, seed=2022, dq_mul=-3.0)
+
+
+def test_single_key_and_uniform_are_exact():
+    """One key: weight 2^6 is exact in E4M3, O = dv * v8[0]; q = 0: every
+    weight is 2^6, O = dv * mean of the visible v8 rows."""
+    q, k, v, ds = synth.fp8_inputs(2, 2, 1, 128, seed=2030, device=DEV)
+    o, _ = fa.fwd_fp8(q, k, v, q_descale=ds, k_descale=ds, v_descale=0.5)
+    torch.cuda.synchronize()
+    vf = v.view(torch.float8_e4m3fn).float()
+    np.testing.assert_allclose(o.cpu().numpy(), 0.5 * vf.cpu().numpy(), rtol=1e-6, atol=1e-6)
+    N = 300
+    _, k, v, ds = synth.fp8_inputs(1, 2, N, 128, seed=2031, device=DEV)
+    q = torch.zeros_like(k)
+    o, lse = fa.fwd_fp8(q, k, v, q_descale=ds, k_descale=ds, v_descale=ds, causal=True)
+    torch.cuda.synchronize()
+    vf = v.view(torch.float8_e4m3fn).double() * ds
+    mean = torch.cumsum(vf, dim=2) / torch.arange(1, N + 1, device=DEV, dtype=torch.float64)[:, None]
+    np.testing.assert_allclose(o.cpu().numpy(), mean.cpu().numpy(), atol=1e-5, rtol=0)
+    np.testing.assert_allclose(lse.cpu().numpy()[0, 0], np.log(np.arange(1, N + 1)), atol=1e-4)
+
+
+def test_lse_optional_and_deterministic():
+    q, k, v, ds = synth.fp8_inputs(2, 2, 500, 128, seed=2040, device=DEV)
+    kw = dict(q_descale=ds, k_descale=ds, v_descale=ds, causal=True)
+    o1, l1 = fa.fwd_fp8(q, k, v, **kw)
+    o2, l2 = fa.fwd_fp8(q, k, v, return_lse=False, **kw)
+    o3, l3 = fa.fwd_fp8(q.view(torch.float8_e4m3fn), k, v, **kw)
+    torch.cuda.synchronize()
+    assert l2 is None
+    assert torch.equal(o1, o2) and torch.equal(o1, o3) and torch.equal(l1, l3)
