@@ -15,6 +15,10 @@ and writes O once.  Timing: W warm-up steps, then K timed steps between a
 synchronize on both sides; HIP events recorded on the launch stream between
 the two calls of every step give each call's average duration.
 
+After the timed steps, the FP8 forward (fa_fwd_fp8) is timed on the same
+forward shape with E4M3 inputs and reported in its own "fp8_fwd" object
+against the dense fp8 MFMA peak; it is not part of the step or of "value".
+
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -35,6 +39,7 @@ if ROOT not in sys.path:
 METRIC = "attn fwd TFLOPS + % MFMA peak (B8 H32 N8192 d128); decode HBM GB/s"
 PEAK_MFMA_TFLOPS = 2516.6     # MI355X dense fp16/bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA (256 CU x 8192 flop/clk x 2.4 GHz)
 FWD = dict(B=8, H=32, N=8192, d=128, dtype="fp16", causal=False, seed=1002)
 DEC = dict(B=8, Hq=32, Hkv=8, L=32768, d=128, dtype="bf16", nsplit=16, seed=1005)
 KV_COPIES = 4                 # decode rotates among this many caches (4 GiB > 256 MB MALL)
@@ -110,12 +115,47 @@ def cpu_baseline(seconds_target=15.0):
             "cpu": platform.processor() or platform.machine()}
 
 
+def time_fp8(fa, synth, stream, steps, warmup):
+    """fa_fwd_fp8 on the forward shape with E4M3 inputs (amp 8, descale 1/8):
+    average launch time from HIP events on the launch stream."""
+    import torch
+    c = FWD
+    q, k, v, ds = synth.fp8_inputs(c["B"], c["H"], c["N"], c["d"], seed=c["seed"],
+                                   device=stream.device)
+    o = torch.empty((c["B"], c["H"], c["N"], c["d"]), dtype=torch.float32, device=stream.device)
+    lse = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device=stream.device)
+    kw = dict(q_descale=ds, k_descale=ds, v_descale=ds, causal=c["causal"],
+              scale=1 / math.sqrt(c["d"]), out=o, lse=lse, stream=stream)
+    for _ in range(warmup):
+        fa.fwd_fp8(q, k, v, **kw)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fa.fwd_fp8(q, k, v, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = fwd_flops(c["B"], c["H"], c["N"], c["d"], c["causal"])
+    tf = flops / (ms * 1e-3) / 1e12
+    digest = source_digest("fa_fwd_fp8.hip", "fa_device.hpp")
+    return {"kernel": "fa_fwd_fp8_kernel", "bound": "mfma", "dtype": "fp8 e4m3",
+            "workload": f"attention forward B{c['B']} H{c['H']} N{c['N']} d{c['d']} fp8 e4m3 "
+                        f"non-causal, per-tensor descale",
+            "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_FP8_TFLOPS, 4), "avg_launch_ms": round(ms, 4),
+            "steps": steps, "traffic": load_traffic("fa_fwd_fp8_kernel", digest),
+            "source_digest": digest}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8-steps", type=int, default=50,
+                    help="timed calls of the FP8 forward on the forward shape (0 skips it)")
     ap.add_argument("--only", choices=["fwd", "decode"], default=None,
                     help="time one call only (for profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -251,6 +291,8 @@ def main():
         "wall_s_timed": round(wall, 3),
         "device": torch.cuda.get_device_name(dev),
     }
+    if args.fp8_steps > 0 and args.only is None:
+        out["fp8_fwd"] = time_fp8(fa, synth, stream, args.fp8_steps, max(5, args.warmup // 2))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
