@@ -17,7 +17,7 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["fwd", "fwd_fp8", "decode", "decode_workspace_bytes", "lib", "FAError", "LIB_PATH",
+__all__ = ["fwd", "fwd_fp8", "decode", "decode_paged", "decode_workspace_bytes", "lib", "FAError", "LIB_PATH",
            "HEADER_PATH", "status_string"]
 
 LIB_PATH = Path(__file__).resolve().parent / "libfa_amd.so"
@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
         L.fa_decode.restype = I
         L.fa_decode_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, I, P, S]
         L.fa_decode_ex.restype = I
+        L.fa_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, I, P, S]
+        L.fa_decode_paged.restype = I
         L.fa_decode_workspace_bytes.argtypes = [I, I, I, I]
         L.fa_decode_workspace_bytes.restype = S
         L.fa_status_string.argtypes = [I]
@@ -183,4 +185,38 @@ def decode(q, kcache, vcache, *, nsplit: int, out=None, lse=None, return_lse: bo
                             Hkv, L, d, int(nsplit), s, _DTYPE[q.dtype], _ptr(workspace),
                             workspace.numel() * workspace.element_size())
     _check(st, "fa_decode_ex")
+    return out, lse
+
+
+def decode_paged(q, kpages, vpages, block_table, seq_lens, *, nsplit: int, out=None, lse=None,
+                 return_lse: bool = True, workspace=None, stream=None):
+    """Split-KV flash-decode over a paged cache.  q: [B, Hq, d];
+    kpages, vpages: [num_pages, page_size, Hkv, d] (bf16/fp16);
+    block_table: [B, pages_per_seq] int32; seq_lens: [B] int32 (all on the GPU).
+    Returns (o [B, Hq, d] fp32, lse [B, Hq] fp32 or None)."""
+    _need(q.dim() == 3 and kpages.dim() == 4 and kpages.shape == vpages.shape,
+          "q must be [B,Hq,d] and the page pools [num_pages,page_size,Hkv,d]")
+    B, Hq, d = q.shape
+    num_pages, page_size, Hkv, dk = kpages.shape
+    _need(dk == d, "head_dim mismatch between q and the page pools")
+    _need(q.dtype in _DTYPE and q.dtype == kpages.dtype == vpages.dtype, "bf16 or fp16 inputs")
+    _need(block_table.dim() == 2 and block_table.shape[0] == B and block_table.dtype == torch.int32,
+          "block_table must be int32 [B, pages_per_seq]")
+    _need(seq_lens.shape == (B,) and seq_lens.dtype == torch.int32, "seq_lens must be int32 [B]")
+    for t in (kpages, vpages, block_table, seq_lens):
+        _need(t.device == q.device and t.is_contiguous(), "contiguous tensors on one GPU")
+    _need(q.is_cuda and q.is_contiguous(), "q must be a contiguous GPU tensor")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = decode_workspace_bytes(B, Hq, d, int(nsplit))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib().fa_decode_paged(_ptr(q), _ptr(kpages), _ptr(vpages), _ptr(block_table),
+                               _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, page_size,
+                               block_table.shape[1], num_pages, d, int(nsplit),
+                               _stream(stream, q.device), _DTYPE[q.dtype], _ptr(workspace),
+                               workspace.numel() * workspace.element_size())
+    _check(st, "fa_decode_paged")
     return out, lse

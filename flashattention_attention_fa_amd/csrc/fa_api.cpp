@@ -181,6 +181,57 @@ fa_status_t fa_decode_ex(const void *q, const void *kcache, const void *vcache, 
     }
 }
 
+fa_status_t fa_decode_paged(const void *q, const void *kpages, const void *vpages,
+                            const int *block_table, const int *seq_lens, float *o, float *lse,
+                            int B, int Hq, int Hkv, int page_size, int pages_per_seq,
+                            int num_pages, int d, int nsplit, hipStream_t stream,
+                            fa_dtype_t dtype, void *workspace, size_t workspace_bytes) {
+    try {
+        if (B < 0 || Hq < 0 || Hkv < 1 || nsplit < 1 || d < 0) return FA_ERR_SHAPE;
+        if (page_size < 16 || page_size % 16 != 0 || pages_per_seq < 1 || num_pages < 1)
+            return FA_ERR_SHAPE;
+        if (B == 0 || Hq == 0) return FA_OK;
+        if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+        if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+        if (!q || !kpages || !vpages || !block_table || !seq_lens || !o) return FA_ERR_NULL;
+        if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+        if (!aligned(q, 16) || !aligned(kpages, 16) || !aligned(vpages, 16) || !aligned(o, 16) ||
+            !aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
+            return FA_ERR_ALIGN;
+        if (B > 65535 || (long long)pages_per_seq * page_size > kMaxSeq) return FA_ERR_SHAPE;
+        const int ncc = (Hq / Hkv + 15) / 16;
+        if ((long long)Hkv * ncc > 65535) return FA_ERR_SHAPE;
+        size_t o_bytes = 0, need = 0;
+        if (!decode_ws_layout(B, Hq, d, nsplit, &o_bytes, &need)) return FA_ERR_SHAPE;
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+            return FA_ERR_WORKSPACE;
+        fa::DecodeArgs a;
+        a.q = q;
+        a.k = kpages;
+        a.v = vpages;
+        a.o = o;
+        a.lse = lse;
+        a.ws_o = static_cast<float *>(workspace);
+        a.ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
+        a.B = B;
+        a.Hq = Hq;
+        a.Hkv = Hkv;
+        a.L = 0;
+        a.d = d;
+        a.nsplit = nsplit;
+        a.chunk = 0;
+        a.dtype = dtype == FA_FP16 ? 1 : 0;
+        a.block_table = block_table;
+        a.seq_lens = seq_lens;
+        a.page_size = page_size;
+        a.pages_per_seq = pages_per_seq;
+        a.num_pages = num_pages;
+        return fa::launch_decode(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    } catch (...) {
+        return FA_ERR_INTERNAL;
+    }
+}
+
 fa_status_t fa_decode(const void *q, const void *kcache, const void *vcache, float *o, int B,
                       int Hq, int Hkv, int L, int d, int nsplit, hipStream_t stream,
                       fa_dtype_t dtype) {

@@ -67,12 +67,21 @@ struct DecBuf {
     u32x4 vr[DecTile<D>::VLOADS];      // V rows, staged to LDS
 };
 
-template <typename T, int D>
+// Paged caches (PAGED): k and v are pools [num_pages, page_size, Hkv, d];
+// sequence b owns seq_lens[b] keys, key j stored in page
+// block_table[b][j / page_size], slot j % page_size.
+struct PagedCache {
+    const int *block_table;   // [B, pages_per_seq]
+    const int *seq_lens;      // [B]
+    int page_size, pages_per_seq, num_pages;
+};
+
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, float *__restrict__ ws_o,
     float *__restrict__ ws_lse, int Hq, int Hkv, int L, int nsplit, int chunk,
-    int ncc, float c) {
+    int ncc, float c, PagedCache pc) {
     typedef DecTile<D> C;
     typedef typename T::vec8 vec8;
     typedef typename T::scalar scalar;
@@ -95,14 +104,34 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
     const int hq0 = g * G + cc * C::COLS;
     const int ncol = min(C::COLS, G - cc * C::COLS);
 
-    const int k_lo = s * chunk;
-    const int k_hi = min(L, k_lo + chunk);
+    // Keys of this sequence and this shard.  Paged: the sequence's own
+    // length (clamped to what its block-table row can address), and shards
+    // of whole 32-key blocks, so that each 16-key half block lies in one page.
+    int Lb = L, chunkb = chunk;
+    if constexpr (PAGED) {
+        Lb = min(max(pc.seq_lens[b], 0), pc.pages_per_seq * pc.page_size);
+        chunkb = (((Lb + nsplit - 1) / nsplit) + C::BK - 1) / C::BK * C::BK;
+    }
+    const int k_lo = min(s * chunkb, Lb);
+    const int k_hi = min(Lb, k_lo + chunkb);
     const int nblk = k_hi > k_lo ? (k_hi - k_lo + C::BK - 1) / C::BK : 0;
 
-    const size_t kvhead = ((size_t)b * Hkv + g) * (size_t)L * D;
-    const uint32_t head_bytes = (uint32_t)L * D * 2;
+    const size_t kvhead = PAGED ? 0 : ((size_t)b * Hkv + g) * (size_t)L * D;
+    const uint32_t head_bytes = PAGED ? 0u : (uint32_t)L * D * 2;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kvhead, head_bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kvhead, head_bytes);
+    // Paged: element offset of the first row of 16-key half block h of the
+    // block at key0 (page of its first key, clamped to the sequence's last
+    // key so masked rows stay inside a valid page; page ids clamped to the
+    // pool).  Rows of a half block are Hkv*D elements apart.
+    const size_t prow = (size_t)Hkv * D;
+    auto half_base = [&](int key0, int h) __attribute__((always_inline)) {
+        const int kh = key0 + 16 * h;
+        const int kc = min(kh, Lb - 1);
+        int pg = pc.block_table[(size_t)b * pc.pages_per_seq + kc / pc.page_size];
+        pg = min(max(pg, 0), pc.num_pages - 1);
+        return ((size_t)pg * pc.page_size + (kh % pc.page_size)) * prow + (size_t)g * D;
+    };
 
     // Q^T fragments: B operand, lane (lj, lg) holds head hq0+lj, dims 32t+8lg..+8.
     vec8 qf[D / 32];
@@ -121,15 +150,31 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
     // are masked out of the softmax below.
     auto load = [&](DecBuf<D> &bf, int n) {
         const int key0 = k_lo + C::BK * n;
+        if constexpr (PAGED) {
+            const size_t hb[2] = {half_base(key0, 0), half_base(key0, 1)};
 #pragma unroll
-        for (int beta = 0; beta < 2; ++beta)
+            for (int beta = 0; beta < 2; ++beta)
 #pragma unroll
-            for (int t = 0; t < D / 32; ++t)
-                bf.kf[beta][t] = buffer_load16_stream(
-                    kr, (uint32_t)((key0 + 16 * beta + lj) * D + 32 * t + 8 * lg) * 2u);
+                for (int t = 0; t < D / 32; ++t)
+                    bf.kf[beta][t] = __builtin_nontemporal_load(
+                        (const u32x4 *)(k + hb[beta] + lj * prow + 32 * t + 8 * lg));
 #pragma unroll
-        for (int r = 0; r < C::VLOADS; ++r)
-            bf.vr[r] = buffer_load16_stream(vr, (uint32_t)((key0 + vrow + C::VROWS * r) * D + 8 * dc) * 2u);
+            for (int r = 0; r < C::VLOADS; ++r) {
+                const int row = vrow + C::VROWS * r;   // row / 16 is static per r
+                bf.vr[r] = __builtin_nontemporal_load(
+                    (const u32x4 *)(v + hb[row >> 4] + (row & 15) * prow + 8 * dc));
+            }
+        } else {
+#pragma unroll
+            for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+                for (int t = 0; t < D / 32; ++t)
+                    bf.kf[beta][t] = buffer_load16_stream(
+                        kr, (uint32_t)((key0 + 16 * beta + lj) * D + 32 * t + 8 * lg) * 2u);
+#pragma unroll
+            for (int r = 0; r < C::VLOADS; ++r)
+                bf.vr[r] = buffer_load16_stream(vr, (uint32_t)((key0 + vrow + C::VROWS * r) * D + 8 * dc) * 2u);
+        }
     };
 
     floatx4 oacc[D / 16];
@@ -321,10 +366,17 @@ static hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
     const int ncc = (G + C::COLS - 1) / C::COLS;
     const float c = kLog2e / sqrtf((float)D);
     if ((long long)a.Hkv * ncc > 65535 || a.B > 65535) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fa_decode_split_kernel<T, D>), dim3(a.nsplit, a.Hkv * ncc, a.B),
-                       dim3(C::THREADS), 0, stream, (const uint16_t *)a.q,
-                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.ws_o, a.ws_lse,
-                       a.Hq, a.Hkv, a.L, a.nsplit, a.chunk, ncc, c);
+    PagedCache pc = {a.block_table, a.seq_lens, a.page_size, a.pages_per_seq, a.num_pages};
+    if (a.block_table != nullptr)
+        hipLaunchKernelGGL((fa_decode_split_kernel<T, D, true>), dim3(a.nsplit, a.Hkv * ncc, a.B),
+                           dim3(C::THREADS), 0, stream, (const uint16_t *)a.q,
+                           (const uint16_t *)a.k, (const uint16_t *)a.v, a.ws_o, a.ws_lse,
+                           a.Hq, a.Hkv, a.L, a.nsplit, a.chunk, ncc, c, pc);
+    else
+        hipLaunchKernelGGL((fa_decode_split_kernel<T, D, false>), dim3(a.nsplit, a.Hkv * ncc, a.B),
+                           dim3(C::THREADS), 0, stream, (const uint16_t *)a.q,
+                           (const uint16_t *)a.k, (const uint16_t *)a.v, a.ws_o, a.ws_lse,
+                           a.Hq, a.Hkv, a.L, a.nsplit, a.chunk, ncc, c, pc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fa_decode_combine_kernel, dim3(a.B * a.Hq), dim3(128), 0, stream,

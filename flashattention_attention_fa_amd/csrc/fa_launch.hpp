@@ -40,6 +40,11 @@ struct DecodeArgs {
     float *ws_lse;          // [B, Hq, nsplit]
     int B, Hq, Hkv, L, d, nsplit, chunk;
     int dtype;
+    // Paged caches (block_table != nullptr): k, v are [num_pages, page_size,
+    // Hkv, d] pools, L is unused, each sequence has seq_lens[b] keys.
+    const int *block_table = nullptr;   // [B, pages_per_seq]
+    const int *seq_lens = nullptr;      // [B]
+    int page_size = 0, pages_per_seq = 0, num_pages = 0;
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

@@ -127,6 +127,32 @@ fa_status_t fa_decode_ex(const void *q, const void *kcache,
                          hipStream_t stream, fa_dtype_t dtype,
                          void *workspace, size_t workspace_bytes);
 
+/*
+ * fa_decode_paged -- fa_decode_ex over a paged key/value cache with a length
+ * per sequence (variable-length batches; the pages mention PagedAttention as
+ * the serving-side cache layout next to FlashAttention).  Sequence b owns
+ * seq_lens[b] cached keys; key j of it lives in page block_table[b][j / P],
+ * slot j % P, of the shared pools
+ *   kpages, vpages : [num_pages, P, Hkv, d] 16-bit, device, 16-byte aligned
+ *   block_table    : [B, pages_per_seq] int32, device
+ *   seq_lens       : [B] int32, device
+ * with P = page_size, a positive multiple of 16.  Shard s of sequence b
+ * covers keys [s*C_b, min(L_b, (s+1)*C_b)) with C_b = ceil(L_b / nsplit)
+ * rounded up to a multiple of 32 (trailing shards may be empty and get
+ * weight 0).  q, o, lse, nsplit, workspace and the definition are those of
+ * fa_decode_ex (workspace from fa_decode_workspace_bytes(B, Hq, d, nsplit));
+ * nsplit is not clamped.  A sequence with no keys gets O = 0 and lse = -inf.
+ * Device-side contents are not validated: lengths are clamped to
+ * [0, pages_per_seq * P] and page ids to [0, num_pages), so bad tables give
+ * wrong results but no out-of-range access.
+ */
+fa_status_t fa_decode_paged(const void *q, const void *kpages, const void *vpages,
+                            const int *block_table, const int *seq_lens, float *o,
+                            float *lse, int B, int Hq, int Hkv, int page_size,
+                            int pages_per_seq, int num_pages, int d, int nsplit,
+                            hipStream_t stream, fa_dtype_t dtype, void *workspace,
+                            size_t workspace_bytes);
+
 /* Static English description of a status code. */
 const char *fa_status_string(fa_status_t status);
 

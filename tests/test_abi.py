@@ -19,7 +19,8 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = fa.declared_functions()
-    assert set(names) >= {"fa_fwd", "fa_fwd_fp8", "fa_decode", "fa_decode_ex", "fa_decode_workspace_bytes",
+    assert set(names) >= {"fa_fwd", "fa_fwd_fp8", "fa_decode", "fa_decode_ex", "fa_decode_paged",
+                          "fa_decode_workspace_bytes",
                           "fa_status_string", "fa_version"}
     for n in names:
         assert hasattr(L, n), n
@@ -71,6 +72,31 @@ def test_fwd_fp8_validation(L):
     assert fwd8(L, dv=float("-inf")) == VALUE
     assert fwd8(L, N=(1 << 23) + 1) == SHAPE
     assert fwd8(L, q=None, k=None, v=None, o=None, B=0) == OK
+
+
+def decp(L, q=A, kp=A, vp=A, bt=A, sl=A, o=A, lse=None, B=1, Hq=4, Hkv=2, page=32, pps=4,
+         npages=8, d=128, nsplit=4, dtype=0, ws=A, ws_bytes=1 << 20):
+    P = ctypes.c_void_p
+    return L.fa_decode_paged(q, kp, vp, P(bt) if bt else None, P(sl) if sl else None, o, lse,
+                             B, Hq, Hkv, page, pps, npages, d, nsplit, None, dtype, ws, ws_bytes)
+
+
+def test_decode_paged_validation(L):
+    assert decp(L, page=0) == SHAPE
+    assert decp(L, page=24) == SHAPE
+    assert decp(L, page=8) == SHAPE
+    assert decp(L, pps=0) == SHAPE
+    assert decp(L, npages=0) == SHAPE
+    assert decp(L, Hkv=3) == SHAPE
+    assert decp(L, bt=None) == NULL
+    assert decp(L, sl=None) == NULL
+    assert decp(L, d=96) == UNSUP
+    assert decp(L, bt=A + 2) == ALIGN
+    assert decp(L, kp=MIS) == ALIGN
+    assert decp(L, ws=None) == WS
+    assert decp(L, ws_bytes=16) == WS
+    assert decp(L, pps=1 << 20, page=16) == SHAPE
+    assert decp(L, q=None, B=0) == OK
 
 
 def test_fwd_empty_is_noop(L):
