@@ -17,7 +17,7 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["fwd", "fwd_fp8", "decode", "decode_paged", "decode_workspace_bytes", "lib", "FAError", "LIB_PATH",
+__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "decode", "decode_paged", "decode_workspace_bytes", "lib", "FAError", "LIB_PATH",
            "HEADER_PATH", "status_string"]
 
 LIB_PATH = Path(__file__).resolve().parent / "libfa_amd.so"
@@ -42,6 +42,8 @@ def lib() -> ctypes.CDLL:
         P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P, I]
         L.fa_fwd.restype = I
+        L.fa_fwd_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, P, I]
+        L.fa_fwd_varlen.restype = I
         L.fa_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, F, F, F, F, P]
         L.fa_fwd_fp8.restype = I
         L.fa_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, P, I]
@@ -113,6 +115,37 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
     st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                       int(bool(causal)), float(scale), _stream(stream, q.device), _DTYPE[q.dtype])
     _check(st, "fa_fwd")
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, *, causal: bool = False,
+               scale: float | None = None, out=None, lse=None, return_lse: bool = True,
+               stream=None):
+    """Attention over a packed batch of variable-length sequences.
+    q, k, v: [T, H, d] bf16/fp16; cu_seqlens: [B+1] int32 on the GPU (sequence
+    b = rows cu[b]..cu[b+1]); max_seqlen: host int >= every length.
+    Returns (o [T, H, d] fp32, lse [H, T] fp32 or None)."""
+    _need(q.dim() == 3 and q.shape == k.shape == v.shape, "q, k, v must share a [T,H,d] shape")
+    _need(q.dtype in _DTYPE and q.dtype == k.dtype == v.dtype, "q, k, v must all be bf16 or fp16")
+    _need(cu_seqlens.dim() == 1 and cu_seqlens.dtype == torch.int32 and cu_seqlens.numel() >= 1,
+          "cu_seqlens must be int32 [B+1]")
+    for t in (k, v, cu_seqlens):
+        _need(t.device == q.device and t.is_contiguous(), "contiguous tensors on one GPU")
+    _need(q.is_cuda and q.is_contiguous(), "q must be a contiguous GPU tensor")
+    T, H, d = q.shape
+    B = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((T, H, d), dtype=torch.float32, device=q.device)
+    _need(out.shape == q.shape and out.dtype == torch.float32 and out.is_contiguous(),
+          "out must be a contiguous fp32 [T,H,d] tensor")
+    if lse is None and return_lse:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    st = lib().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
+                             B, H, T, int(max_seqlen), d, int(bool(causal)), float(scale),
+                             _stream(stream, q.device), _DTYPE[q.dtype])
+    _check(st, "fa_fwd_varlen")
     return out, lse
 
 

@@ -121,6 +121,44 @@ fa_status_t fa_fwd(const void *q, const void *k, const void *v, float *o, float 
     }
 }
 
+fa_status_t fa_fwd_varlen(const void *q, const void *k, const void *v, float *o, float *lse,
+                          const int *cu_seqlens, int B, int H, int total_tokens, int max_seqlen,
+                          int d, int causal, float scale, hipStream_t stream, fa_dtype_t dtype) {
+    try {
+        if (B < 0 || H < 0 || total_tokens < 0 || max_seqlen < 0 || d < 0) return FA_ERR_SHAPE;
+        if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+        if (!std::isfinite(scale)) return FA_ERR_VALUE;
+        if (B == 0 || H == 0 || total_tokens == 0 || max_seqlen == 0) return FA_OK;
+        if (!q || !k || !v || !o || !cu_seqlens) return FA_ERR_NULL;
+        if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+            !aligned(cu_seqlens, 4) || (lse && !aligned(lse, 4)))
+            return FA_ERR_ALIGN;
+        const long long BH = (long long)B * H;
+        if ((long long)max_seqlen * H * d >= (1ll << 30) || BH > INT_MAX ||
+            BH * ((max_seqlen + 127) / 128) > INT_MAX)
+            return FA_ERR_SHAPE;
+        fa::FwdArgs a;
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.o = o;
+        a.lse = lse;
+        a.BH = (int)BH;
+        a.N = max_seqlen;
+        a.d = d;
+        a.causal = causal != 0;
+        a.scale = scale;
+        a.dtype = dtype == FA_FP16 ? 1 : 0;
+        a.cu_seqlens = cu_seqlens;
+        a.H = H;
+        a.T = total_tokens;
+        return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    } catch (...) {
+        return FA_ERR_INTERNAL;
+    }
+}
+
 fa_status_t fa_fwd_fp8(const void *q, const void *k, const void *v, float *o, float *lse,
                        int B, int H, int N, int d, int causal, float scale, float q_descale,
                        float k_descale, float v_descale, hipStream_t stream) {

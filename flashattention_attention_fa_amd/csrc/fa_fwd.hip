@@ -97,11 +97,19 @@ __device__ __forceinline__ int swz_v(int r) {
 // of a tile is computed only on that rare path.
 constexpr float kTileSumLimit = 1024.0f;
 
-template <typename T, int D, bool CAUSAL>
+// Packed variable-length batches (VARLEN): q, k, v, o are [T, H, D] with
+// sequence b at rows [cu[b], cu[b+1]); lse is [H, T].
+struct Varlen {
+    const int *cu;   // [B + 1]
+    int H, T;
+};
+
+template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, float *__restrict__ o,
-    float *__restrict__ lse, int N, int nq, float c, uint32_t qand, uint32_t qxor) {
+    float *__restrict__ lse, int Nmax, int nq, float c, uint32_t qand, uint32_t qxor,
+    Varlen vl) {
     typedef FwdTile<D, CAUSAL> C;
     static_assert(C::THREADS == (CAUSAL ? 256 : 512) && C::BLOCKS_PER_CU == (CAUSAL ? 2 : 1),
                   "launch bounds must match the tile shape");
@@ -132,10 +140,25 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_ker
     const unsigned id = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = (int)(id / (unsigned)nq);
     const int qt = CAUSAL ? nq - 1 - (int)(id % (unsigned)nq) : (int)(id % (unsigned)nq);
-    const size_t head = (size_t)bh * N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + head, head_bytes);
     const int q0 = qt * BM;
+    // This (sequence, head): N keys = N queries, row 0 at element `head`,
+    // consecutive rows RS elements apart, lse of row i at lse_row0 + i.
+    // Varlen: bounds read from cu are clamped to [0, T] and to Nmax, and
+    // workgroups past the sequence end leave at once (before any barrier).
+    int N = Nmax;
+    size_t head = (size_t)bh * Nmax * D, lse_row0 = (size_t)bh * Nmax;
+    const int RS = VARLEN ? vl.H * D : D;
+    if constexpr (VARLEN) {
+        const int b = bh / vl.H, h = bh % vl.H;
+        const int s0 = min(max(vl.cu[b], 0), vl.T);
+        const int e = min(max(vl.cu[b + 1], s0), vl.T);
+        N = min(e - s0, Nmax);
+        head = ((size_t)s0 * vl.H + h) * D;
+        lse_row0 = (size_t)h * vl.T + s0;
+        if (q0 >= N) return;
+    }
+    const uint32_t head_bytes = (uint32_t)((N > 0 ? (size_t)(N - 1) * RS + D : 0) * 2);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + head, head_bytes);
     const int qw = q0 + wave * 32;    // first query of this wave
     const int my_q = qw + li;
 
@@ -144,7 +167,7 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_ker
     vec8 qf[KSTEPS];
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
-        u32x4 x = buffer_load16(qr, (uint32_t)(my_q * D + 16 * t + 8 * lh) * 2u);
+        u32x4 x = buffer_load16(qr, (uint32_t)(my_q * RS + 16 * t + 8 * lh) * 2u);
         // scale < 0: flip the sign of q (exact) and use |scale|;
         // scale == 0: every visible score is 0, i.e. q = 0.
         x = (x & qand) ^ qxor;
@@ -165,14 +188,14 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_ker
     for (int i = 0; i < C::LOADS; ++i) {
         const int row = wave * C::ROWS + i * C::RPI + lane / KCH;
         const int pos = lane % KCH;
-        koff[i] = (uint32_t)(row * D + 8 * (pos ^ swz_k<D>(row))) * 2u;
-        voff[i] = (uint32_t)(row * D + 8 * (pos ^ swz_v<D>(row))) * 2u;
+        koff[i] = (uint32_t)(row * RS + 8 * (pos ^ swz_k<D>(row))) * 2u;
+        voff[i] = (uint32_t)(row * RS + 8 * (pos ^ swz_v<D>(row))) * 2u;
     }
     // The tile's base goes into the (scalar) buffer resource, so the
     // per-lane offsets stay fixed and the range check still covers the end of
     // the head: a resource past the end has zero records and reads zeros.
     auto tile_rsrc = [&](const uint16_t *base, int tile) __attribute__((always_inline)) {
-        const uint32_t off = (uint32_t)tile * (BN * D * 2);
+        const uint32_t off = (uint32_t)tile * (uint32_t)(BN * RS * 2);
         const uint64_t addr = (uint64_t)(uintptr_t)base + off;
         // Uniform values: keep the resource in scalar registers.
         const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
@@ -406,7 +429,7 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_ker
     const float l_tot = sum_halves(l_run);
     if (my_q < N) {
         const float inv = 1.f / l_tot;
-        float *orow = o + head + (size_t)my_q * D + 4 * lh;
+        float *orow = o + head + (size_t)my_q * RS + 4 * lh;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -415,23 +438,31 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_ker
                     floatx4{oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv,
                             oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv};
         if (lse != nullptr && lh == 0)
-            lse[(size_t)bh * N + my_q] = (m_run + log2f(l_tot)) * kLn2;
+            lse[lse_row0 + my_q] = (m_run + log2f(l_tot)) * kLn2;
     }
 }
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch(const FwdArgs &a, hipStream_t stream) {
     typedef FwdTile<D, CAUSAL> C;
-    const int nq = (a.N + C::BM - 1) / C::BM;
+    const int nq = (a.N + C::BM - 1) / C::BM;   // N = longest sequence when varlen
     const long long blocks = (long long)nq * a.BH;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const bool zero = a.scale == 0.f;
     const float c = zero ? kLog2e : fabsf(a.scale) * kLog2e;
     const uint32_t qand = zero ? 0u : 0xffffffffu;
     const uint32_t qxor = a.scale < 0.f ? 0x80008000u : 0u;
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(C::THREADS),
-                       0, stream, (const uint16_t *)a.q, (const uint16_t *)a.k,
-                       (const uint16_t *)a.v, a.o, a.lse, a.N, nq, c, qand, qxor);
+    const Varlen vl = {a.cu_seqlens, a.H, a.T};
+    if (a.cu_seqlens != nullptr)
+        hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, true>), dim3((unsigned)blocks),
+                           dim3(C::THREADS), 0, stream, (const uint16_t *)a.q,
+                           (const uint16_t *)a.k, (const uint16_t *)a.v, a.o, a.lse, a.N, nq, c,
+                           qand, qxor, vl);
+    else
+        hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, false>), dim3((unsigned)blocks),
+                           dim3(C::THREADS), 0, stream, (const uint16_t *)a.q,
+                           (const uint16_t *)a.k, (const uint16_t *)a.v, a.o, a.lse, a.N, nq, c,
+                           qand, qxor, vl);
     return hipGetLastError();
 }
 

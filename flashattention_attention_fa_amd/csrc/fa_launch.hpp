@@ -15,6 +15,10 @@ struct FwdArgs {
     bool causal;
     float scale;
     int dtype;              // 0 bf16, 1 fp16
+    // Packed variable-length batch (cu_seqlens != nullptr): q, k, v, o are
+    // [T, H, d], BH = B*H, N = the longest sequence, lse is [H, T].
+    const int *cu_seqlens = nullptr;   // [B + 1]
+    int H = 0, T = 0;
 };
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);

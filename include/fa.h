@@ -62,6 +62,31 @@ fa_status_t fa_fwd(const void *q, const void *k, const void *v, float *o,
                    float scale, hipStream_t stream, fa_dtype_t dtype);
 
 /*
+ * fa_fwd_varlen -- fa_fwd over a packed batch of sequences of different
+ * lengths (jagged / variable-length attention; the "jagged attention" item
+ * of the roadmap in the Triton warp-specialisation note).  Sequence b is
+ * rows [cu_seqlens[b], cu_seqlens[b+1]) of the packed tensors and attends
+ * only to itself (causal: key j visible to query i iff j <= i, both counted
+ * within the sequence).
+ *
+ *   q, k, v    : [total_tokens, H, d] 16-bit, device, 16-byte aligned
+ *   o          : [total_tokens, H, d] fp32, device, 16-byte aligned
+ *   lse        : [H, total_tokens] fp32, device, or NULL
+ *   cu_seqlens : [B + 1] int32, device: 0 = cu[0] <= cu[1] <= ... <= cu[B]
+ *                = total_tokens
+ *   max_seqlen : >= every cu[b+1] - cu[b] (host value; sizes the grid)
+ *   d          : 64 or 128;  max_seqlen * H * d < 2^30 (else FA_ERR_SHAPE)
+ * Device-side cu_seqlens are not validated: offsets are clamped to
+ * [0, total_tokens] and lengths to max_seqlen, so a bad table gives wrong
+ * results but no out-of-range access.  B == 0, H == 0 or total_tokens == 0
+ * is a no-op returning FA_OK.
+ */
+fa_status_t fa_fwd_varlen(const void *q, const void *k, const void *v, float *o,
+                          float *lse, const int *cu_seqlens, int B, int H,
+                          int total_tokens, int max_seqlen, int d, int causal,
+                          float scale, hipStream_t stream, fa_dtype_t dtype);
+
+/*
  * fa_fwd_fp8 -- fa_fwd for FP8 inputs with per-tensor dequantization
  * factors: the FP8 variant of the tiled forward that the dailyaiworld page
  * features (introduction and pipeline figure).  q, k, v hold OCP E4M3

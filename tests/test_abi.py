@@ -19,7 +19,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = fa.declared_functions()
-    assert set(names) >= {"fa_fwd", "fa_fwd_fp8", "fa_decode", "fa_decode_ex", "fa_decode_paged",
+    assert set(names) >= {"fa_fwd", "fa_fwd_varlen", "fa_fwd_fp8", "fa_decode", "fa_decode_ex", "fa_decode_paged",
                           "fa_decode_workspace_bytes",
                           "fa_status_string", "fa_version"}
     for n in names:
@@ -97,6 +97,27 @@ def test_decode_paged_validation(L):
     assert decp(L, ws_bytes=16) == WS
     assert decp(L, pps=1 << 20, page=16) == SHAPE
     assert decp(L, q=None, B=0) == OK
+
+
+def fwdv(L, q=A, k=A, v=A, o=A, lse=None, cu=A, B=2, H=2, T=64, maxs=32, d=128, causal=0,
+         scale=0.1, dtype=0):
+    return L.fa_fwd_varlen(q, k, v, o, lse, ctypes.c_void_p(cu) if cu else None, B, H, T, maxs,
+                           d, causal, scale, None, dtype)
+
+
+def test_fwd_varlen_validation(L):
+    assert fwdv(L, cu=None) == NULL
+    assert fwdv(L, q=None) == NULL
+    assert fwdv(L, B=-1) == SHAPE
+    assert fwdv(L, maxs=-1) == SHAPE
+    assert fwdv(L, d=80) == UNSUP
+    assert fwdv(L, dtype=5) == UNSUP
+    assert fwdv(L, cu=A + 2) == ALIGN
+    assert fwdv(L, o=MIS) == ALIGN
+    assert fwdv(L, scale=float("nan")) == VALUE
+    assert fwdv(L, maxs=1 << 22, H=4) == SHAPE
+    assert fwdv(L, q=None, k=None, v=None, o=None, cu=None, B=0) == OK
+    assert fwdv(L, q=None, k=None, v=None, o=None, cu=None, T=0) == OK
 
 
 def test_fwd_empty_is_noop(L):
