@@ -137,9 +137,17 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_ker
     // one head, so the workgroups resident on one XCD share that head's K/V
     // in their L2.  Causal: each head's q-tiles run longest (most keys) first,
     // so the short ones fill the tail.
+    // Varlen: sequences differ in length, and each XCD takes a contiguous
+    // range of (sequence, head) pairs, so the pairs are ordered head-major
+    // across sequences: every XCD gets an equal share of every sequence's
+    // heads, while the q-tiles of one head stay together on one XCD.
     const unsigned id = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = (int)(id / (unsigned)nq);
+    int bh = (int)(id / (unsigned)nq);
     const int qt = CAUSAL ? nq - 1 - (int)(id % (unsigned)nq) : (int)(id % (unsigned)nq);
+    if constexpr (VARLEN) {
+        const int nseq = (int)(gridDim.x / (unsigned)nq) / vl.H;
+        bh = (bh % nseq) * vl.H + bh / nseq;
+    }
     const int q0 = qt * BM;
     // This (sequence, head): N keys = N queries, row 0 at element `head`,
     // consecutive rows RS elements apart, lse of row i at lse_row0 + i.
