@@ -49,6 +49,14 @@ def fwd_inputs(B, H, N, d, dtype="bf16", seed=0, device="cpu",
     return q, k, v
 
 
+def bwd_inputs(B, H, N, d, dtype="bf16", seed=0, device="cpu"):
+    """q, k, v as fwd_inputs, plus the upstream gradient dout [B, H, N, d]
+    (i.i.d. N(0, 1), seed seed*16 + 4, rounded to the storage type)."""
+    q, k, v = fwd_inputs(B, H, N, d, dtype, seed, device)
+    dout = normal((B, H, N, d), int(seed) * 16 + 4, dtype, device)
+    return q, k, v, dout
+
+
 def fp8_inputs(B, H, N, d, seed=0, device="cpu", amp=8.0):
     """FP8 (E4M3) q, k, v of shape [B, H, N, d] as uint8 tensors holding the
     E4M3 bytes, and their per-tensor dequantization factor 1/amp: each

@@ -1,6 +1,6 @@
 /*
- * fa_oracle.c -- the fp64 CPU oracle for exact attention and its split-KV
- * (partial output + log-sum-exp) combine.
+ * fa_oracle.c -- the fp64 CPU oracle for exact attention, its split-KV
+ * (partial output + log-sum-exp) combine, and its gradients.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
  * call this file: only the test suite, the package smoke check and the CPU
@@ -30,6 +30,11 @@
  *    softmax denominator; each shard must carry its log-sum-exp, and the
  *    combine re-normalises the partial outputs with it.  oracle_combine()
  *    is that re-normalisation written out.
+ *
+ *  - "Warp Specialization in Triton: Design and Roadmap" (PyTorch blog),
+ *    roadmap section: the attention backward is the next kernel.  Its oracle
+ *    (oracle_attention_bwd) is the chain rule applied to the definition
+ *    above, written out term by term.
  *
  * Readings where the pages are silent (each one is listed in the design
  * notes): causal means key j is visible to query i iff j <= i; the
@@ -337,5 +342,259 @@ int oracle_decode(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
                                    1.0 / sqrt((double)d), 0, L, rows, n,
                                    out_o, out_lse);
     free(rows);
+    return rc;
+}
+
+/*
+ * ---------------------------------------------------------------------------
+ * Gradients of attention (the backward pass).
+ *
+ * "Warp Specialization in Triton: Design and Roadmap" (PyTorch blog), section
+ * on what is still missing by the authors' own roadmap: the attention
+ * backward is the next kernel after the forward.  The pages give no formula
+ * for it, so the oracle is the chain rule applied to the definition above,
+ * for self-attention (Nq = Nk = N, one key/value head per query head).  With
+ * P_ij = exp(s_ij - lse_i) on the keys visible to query i (0 elsewhere),
+ * O_i = sum_j P_ij v_j and an upstream gradient dO:
+ *     dV_j  = sum_i P_ij dO_i
+ *     dP_ij = <dO_i, v_j>
+ *     dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)        (softmax Jacobian)
+ *     dQ_i  = scale * sum_j dS_ij k_j
+ *     dK_j  = scale * sum_i dS_ij q_i
+ * A query with no visible key has no weights and contributes nothing.
+ *
+ * Inputs are bit patterns of dtype (bf16, fp16), or, with ORACLE_F64, plain
+ * doubles: the finite-difference pin perturbs inputs continuously.
+ * ---------------------------------------------------------------------------
+ */
+#define ORACLE_F64 3
+
+static double elem_at(const void *p, long idx, int dtype)
+{
+    if (dtype == ORACLE_F64)
+        return ((const double *)p)[idx];
+    return oracle_widen(((const uint16_t *)p)[idx], dtype);
+}
+
+/* Per-row statistics of one head: lse_i and Dl_i = sum_k P_ik dP_ik, plus
+ * O_i when o is not NULL.  Rows run in parallel. */
+static int head_row_stats(const double *q, const double *k, const double *v,
+                          const double *dout, long N, long d, int causal,
+                          double scale, double *lse, double *dl, double *o)
+{
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        double *oi = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!s || !oi) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (long i = 0; i < N; ++i) {
+            if (!s || !oi)
+                continue;
+            double m = -INFINITY;
+            for (long j = 0; j < N; ++j) {
+                if (!key_visible(j, i, causal))
+                    continue;
+                double dot = 0.0;
+                for (long c = 0; c < d; ++c)
+                    dot += q[i * d + c] * k[j * d + c];
+                s[j] = scale * dot;
+                if (s[j] > m)
+                    m = s[j];
+            }
+            for (long c = 0; c < d; ++c)
+                oi[c] = 0.0;
+            if (m == -INFINITY) {
+                lse[i] = -INFINITY;
+                dl[i] = 0.0;
+                if (o)
+                    for (long c = 0; c < d; ++c)
+                        o[i * d + c] = 0.0;
+                continue;
+            }
+            double l = 0.0;
+            for (long j = 0; j < N; ++j)
+                if (key_visible(j, i, causal))
+                    l += exp(s[j] - m);
+            const double L = m + log(l);
+            /* sum_k P_ik dP_ik, and O_i */
+            double acc = 0.0;
+            for (long j = 0; j < N; ++j) {
+                if (!key_visible(j, i, causal))
+                    continue;
+                double p = exp(s[j] - L);
+                double dp = 0.0;
+                for (long c = 0; c < d; ++c) {
+                    dp += dout[i * d + c] * v[j * d + c];
+                    oi[c] += p * v[j * d + c];
+                }
+                acc += p * dp;
+            }
+            lse[i] = L;
+            dl[i] = acc;
+            if (o)
+                for (long c = 0; c < d; ++c)
+                    o[i * d + c] = oi[c];
+        }
+        free(s);
+        free(oi);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Selected gradients of a [B, H, N, d] problem.
+ *   q, k, v, dout  [B, H, N, d] of dtype (bits, or doubles with ORACLE_F64)
+ *   qrows          nq triples (b, h, i): rows of dQ (and of O, lse) wanted
+ *   kcols          nk triples (b, h, j): rows of dK and dV wanted
+ *   out_dq [nq, d], out_o [nq, d] (may be NULL), out_lse [nq] (may be NULL),
+ *   out_dk, out_dv [nk, d]
+ * Returns 0, or -1 on a bad argument or allocation failure.
+ */
+int oracle_attention_bwd(const void *q, const void *k, const void *v,
+                         const void *dout, int dtype, long B, long H, long N,
+                         long d, int causal, double scale, const long *qrows,
+                         long nq, const long *kcols, long nk, double *out_dq,
+                         double *out_o, double *out_lse, double *out_dk,
+                         double *out_dv)
+{
+    if (!q || !k || !v || !dout || (nq && (!qrows || !out_dq)) ||
+        (nk && (!kcols || !out_dk || !out_dv)))
+        return -1;
+    if (B < 0 || H < 1 || N < 0 || d < 1 || nq < 0 || nk < 0)
+        return -1;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_FP16 && dtype != ORACLE_F64)
+        return -1;
+    for (long r = 0; r < nq + nk; ++r) {
+        const long *t = r < nq ? qrows + 3 * r : kcols + 3 * (r - nq);
+        if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= H || t[2] < 0 || t[2] >= N)
+            return -1;
+    }
+    const size_t nd = (size_t)N * (size_t)d;
+    double *hq = (double *)malloc(sizeof(double) * (nd ? nd : 1));
+    double *hk = (double *)malloc(sizeof(double) * (nd ? nd : 1));
+    double *hv = (double *)malloc(sizeof(double) * (nd ? nd : 1));
+    double *hdo = (double *)malloc(sizeof(double) * (nd ? nd : 1));
+    double *lse = (double *)malloc(sizeof(double) * (size_t)(N ? N : 1));
+    double *dl = (double *)malloc(sizeof(double) * (size_t)(N ? N : 1));
+    double *ho = out_o ? (double *)malloc(sizeof(double) * (nd ? nd : 1)) : NULL;
+    int rc = 0;
+    if (!hq || !hk || !hv || !hdo || !lse || !dl || (out_o && !ho))
+        rc = -1;
+
+    /* One head at a time: every head named by either list. */
+    for (long bh = 0; rc == 0 && bh < B * H; ++bh) {
+        long b = bh / H, h = bh % H;
+        int needed = 0;
+        for (long r = 0; r < nq + nk && !needed; ++r) {
+            const long *t = r < nq ? qrows + 3 * r : kcols + 3 * (r - nq);
+            needed = t[0] == b && t[1] == h;
+        }
+        if (!needed)
+            continue;
+        const long base = bh * (long)nd;
+        for (size_t e = 0; e < nd; ++e) {
+            hq[e] = elem_at(q, base + (long)e, dtype);
+            hk[e] = elem_at(k, base + (long)e, dtype);
+            hv[e] = elem_at(v, base + (long)e, dtype);
+            hdo[e] = elem_at(dout, base + (long)e, dtype);
+        }
+        if (head_row_stats(hq, hk, hv, hdo, N, d, causal, scale, lse, dl, ho)) {
+            rc = -1;
+            break;
+        }
+
+        /* dQ_i = scale * sum_j P_ij (dP_ij - Dl_i) k_j */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (long r = 0; r < nq; ++r) {
+            const long *t = qrows + 3 * r;
+            if (t[0] != b || t[1] != h)
+                continue;
+            const long i = t[2];
+            double *g = out_dq + r * d;
+            for (long c = 0; c < d; ++c)
+                g[c] = 0.0;
+            if (out_o)
+                for (long c = 0; c < d; ++c)
+                    out_o[r * d + c] = ho[i * d + c];
+            if (out_lse)
+                out_lse[r] = lse[i];
+            if (lse[i] == -INFINITY)
+                continue;
+            for (long j = 0; j < N; ++j) {
+                if (!key_visible(j, i, causal))
+                    continue;
+                double dot = 0.0, dp = 0.0;
+                for (long c = 0; c < d; ++c) {
+                    dot += hq[i * d + c] * hk[j * d + c];
+                    dp += hdo[i * d + c] * hv[j * d + c];
+                }
+                const double p = exp(scale * dot - lse[i]);
+#if ORACLE_MUTANT == 15
+                const double ds = p * dp;
+#else
+                const double ds = p * (dp - dl[i]);
+#endif
+                for (long c = 0; c < d; ++c)
+                    g[c] += ds * hk[j * d + c];
+            }
+#if ORACLE_MUTANT != 16
+            for (long c = 0; c < d; ++c)
+                g[c] *= scale;
+#endif
+        }
+
+        /* dV_j = sum_i P_ij dO_i;  dK_j = scale * sum_i dS_ij q_i */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (long r = 0; r < nk; ++r) {
+            const long *t = kcols + 3 * r;
+            if (t[0] != b || t[1] != h)
+                continue;
+            const long j = t[2];
+            double *gk = out_dk + r * d, *gv = out_dv + r * d;
+            for (long c = 0; c < d; ++c)
+                gk[c] = gv[c] = 0.0;
+            for (long i = 0; i < N; ++i) {
+#if ORACLE_MUTANT == 19
+                if (lse[i] == -INFINITY)
+#else
+                if (!key_visible(j, i, causal) || lse[i] == -INFINITY)
+#endif
+                    continue;
+                double dot = 0.0, dp = 0.0;
+                for (long c = 0; c < d; ++c) {
+                    dot += hq[i * d + c] * hk[j * d + c];
+                    dp += hdo[i * d + c] * hv[j * d + c];
+                }
+#if ORACLE_MUTANT == 17
+                const double p = exp(scale * dot);
+#else
+                const double p = exp(scale * dot - lse[i]);
+#endif
+                const double ds = p * (dp - dl[i]);
+                for (long c = 0; c < d; ++c) {
+                    gv[c] += p * hdo[i * d + c];
+#if ORACLE_MUTANT == 18
+                    gk[c] += ds * hdo[i * d + c];
+#else
+                    gk[c] += ds * hq[i * d + c];
+#endif
+                }
+            }
+            for (long c = 0; c < d; ++c)
+                gk[c] *= scale;
+        }
+    }
+    free(hq);
+    free(hk);
+    free(hv);
+    free(hdo);
+    free(lse);
+    free(dl);
+    free(ho);
     return rc;
 }

@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for exact attention, split-KV partials and their combine.
+"""fp64 CPU oracle for exact attention, split-KV partials and their combine,
+and the gradients of attention.
 
 TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the
 benchmark's CPU-baseline leg are the only callers.  The product path never
@@ -66,6 +67,9 @@ class Oracle:
         self.lib.oracle_decode.restype = I
         self.lib.oracle_widen.argtypes = [ctypes.c_uint16, I]
         self.lib.oracle_widen.restype = D
+        self.lib.oracle_attention_bwd.argtypes = [P, P, P, P, I, L, L, L, L, I, D, P, L, P, L,
+                                                  P, P, P, P, P]
+        self.lib.oracle_attention_bwd.restype = I
 
     # -- helpers -----------------------------------------------------------
     @staticmethod
@@ -175,6 +179,49 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_decode rejected its arguments")
         return o, lse
+
+    # -- gradients -----------------------------------------------------------
+    def attention_bwd(self, q, k, v, dout, dtype: str, causal: bool, scale: float,
+                      qrows=None, kcols=None):
+        """Gradients of self-attention with upstream gradient ``dout``.
+
+        q, k, v, dout: [B,H,N,d] uint16 bit patterns of ``dtype``, or float64
+        arrays with ``dtype="f64"``.  qrows / kcols: (n,3) arrays of
+        (b, h, i); None means every row.  Returns a dict with dq, o, lse (for
+        qrows) and dk, dv (for kcols); with both None the arrays have the
+        shapes [B,H,N,d] and [B,H,N]."""
+        if dtype == "f64":
+            code = 3
+            arrs = [np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v, dout)]
+        else:
+            code = DTYPES[dtype]
+            arrs = [self._bits(a) for a in (q, k, v, dout)]
+        q, k, v, dout = arrs
+        if not (q.shape == k.shape == v.shape == dout.shape) or q.ndim != 4:
+            raise ValueError("shape mismatch")
+        B, H, N, d = q.shape
+        full = qrows is None and kcols is None
+        bb, hh, ii = np.meshgrid(np.arange(B), np.arange(H), np.arange(N), indexing="ij")
+        every = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
+        qrows = every if qrows is None else qrows
+        kcols = every if kcols is None else kcols
+        qrows = np.ascontiguousarray(np.asarray(qrows, dtype=np.int64).reshape(-1, 3))
+        kcols = np.ascontiguousarray(np.asarray(kcols, dtype=np.int64).reshape(-1, 3))
+        nq, nk = qrows.shape[0], kcols.shape[0]
+        dq = np.zeros((nq, d)); o = np.zeros((nq, d)); lse = np.zeros(nq)
+        dk = np.zeros((nk, d)); dv = np.zeros((nk, d))
+        rc = self.lib.oracle_attention_bwd(
+            self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(dout), code, B, H, N, d,
+            int(bool(causal)), float(scale), self._ptr(qrows), nq, self._ptr(kcols), nk,
+            self._ptr(dq), self._ptr(o), self._ptr(lse), self._ptr(dk), self._ptr(dv))
+        if rc != 0:
+            raise ValueError("oracle_attention_bwd rejected its arguments")
+        out = {"dq": dq, "o": o, "lse": lse, "dk": dk, "dv": dv}
+        if full:
+            for key in ("dq", "o", "dk", "dv"):
+                out[key] = out[key].reshape(B, H, N, d)
+            out["lse"] = lse.reshape(B, H, N)
+        return out
 
 
 _default: Oracle | None = None

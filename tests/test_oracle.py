@@ -314,10 +314,109 @@ def pin_fp8_single_key(orc):
     np.testing.assert_allclose(lse, want, rtol=1e-13)
 
 
+# -- gradients ---------------------------------------------------------------
+
+def pin_bwd_finite_difference(orc):
+    """Central differences of f = sum(dout * O) with respect to every input
+    element, on fp64 inputs (no storage rounding), with and without the
+    causal mask."""
+    rng = np.random.default_rng(31)
+    B, H, N, d, h = 1, 2, 6, 4, 1e-5
+    for causal in (False, True):
+        q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+        g = orc.attention_bwd(q, k, v, do, "f64", causal, 0.7)
+
+        def f(qq, kk, vv):
+            return float((orc.attention_bwd(qq, kk, vv, do, "f64", causal, 0.7)["o"] * do).sum())
+
+        for name, which in (("dq", 0), ("dk", 1), ("dv", 2)):
+            num = np.zeros((B, H, N, d))
+            for idx in np.ndindex(B, H, N, d):
+                args_p = [q.copy(), k.copy(), v.copy()]
+                args_m = [q.copy(), k.copy(), v.copy()]
+                args_p[which][idx] += h
+                args_m[which][idx] -= h
+                num[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+            np.testing.assert_allclose(g[name], num, rtol=0, atol=1e-7,
+                                       err_msg=f"{name} causal={causal}")
+
+
+def pin_bwd_library_routine(orc):
+    """torch autograd through CPU fp64 scaled_dot_product_attention."""
+    for dtype, causal, shape, scale in (("bf16", False, (1, 2, 40, 64), 0.125),
+                                        ("fp16", True, (2, 1, 37, 32), 1 / math.sqrt(32))):
+        q, k, v, do = synth.bwd_inputs(*shape, dtype, seed=32)
+        bits = [synth.to_bits(t) for t in (q, k, v, do)]
+        g = orc.attention_bwd(*bits, dtype, causal, scale)
+        tq, tk, tv, tdo = (torch.from_numpy(widened(b, dtype)) for b in bits)
+        for t in (tq, tk, tv):
+            t.requires_grad_(True)
+        o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                             scale=scale)
+        (o * tdo).sum().backward()
+        for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+            np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=1e-9, atol=1e-11,
+                                       err_msg=name)
+
+
+def pin_bwd_invariants(orc):
+    """Every row of dS sums to zero, so sum_j dK_j = 0; the weights of each
+    query sum to one, so sum_j dV_j = sum_i dO_i; and scaling every score by
+    t gives d/dt = sum_i <dQ_i, q_i> = sum_j <dK_j, k_j>."""
+    for causal in (False, True):
+        q, k, v, do = synth.bwd_inputs(2, 2, 50, 16, "fp16", seed=33)
+        bits = [synth.to_bits(t) for t in (q, k, v, do)]
+        g = orc.attention_bwd(*bits, "fp16", causal, 0.3)
+        qw, kw, dow = widened(bits[0], "fp16"), widened(bits[1], "fp16"), widened(bits[3], "fp16")
+        np.testing.assert_allclose(g["dk"].sum(axis=2), 0.0, atol=1e-11)
+        np.testing.assert_allclose(g["dv"].sum(axis=2), dow.sum(axis=2), rtol=1e-12, atol=1e-11)
+        np.testing.assert_allclose((g["dq"] * qw).sum(axis=(2, 3)),
+                                   (g["dk"] * kw).sum(axis=(2, 3)), rtol=1e-10, atol=1e-10)
+
+
+def pin_bwd_closed_forms(orc):
+    """One key: the weight is 1 whatever q and k are, so dQ = dK = 0 and
+    dV = dO.  Causal row 0 sees only key 0: dQ_0 = 0.  Value rows all equal:
+    O does not depend on the weights, so dQ = dK = 0."""
+    q, k, v, do = synth.bwd_inputs(1, 2, 1, 8, "bf16", seed=34)
+    bits = [synth.to_bits(t) for t in (q, k, v, do)]
+    g = orc.attention_bwd(*bits, "bf16", False, 0.9)
+    assert not g["dq"].any() and not g["dk"].any()
+    np.testing.assert_array_equal(g["dv"], widened(bits[3], "bf16"))
+    q, k, v, do = synth.bwd_inputs(1, 1, 9, 8, "bf16", seed=35)
+    bits = [synth.to_bits(t) for t in (q, k, v, do)]
+    g = orc.attention_bwd(*bits, "bf16", True, 0.9)
+    assert not g["dq"][0, 0, 0].any()
+    vrow = np.repeat(bits[2][:, :, :1, :], 9, axis=2)
+    g = orc.attention_bwd(bits[0], bits[1], vrow, bits[3], "bf16", False, 0.9)
+    np.testing.assert_allclose(g["dq"], 0.0, atol=1e-13)
+    np.testing.assert_allclose(g["dk"], 0.0, atol=1e-13)
+
+
+def pin_bwd_forward_outputs(orc):
+    """The O and lse the gradient routine recomputes are the forward's, and
+    selected rows and columns equal the same rows of the full result."""
+    q, k, v, do = synth.bwd_inputs(1, 3, 45, 32, "bf16", seed=36)
+    bits = [synth.to_bits(t) for t in (q, k, v, do)]
+    g = orc.attention_bwd(*bits, "bf16", True, 0.2)
+    o, lse = orc.attention(*bits[:3], "bf16", True, 0.2)
+    np.testing.assert_allclose(g["o"], o, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(g["lse"], lse, rtol=1e-13, atol=1e-15)
+    sel = np.array([(0, 2, 44), (0, 0, 0), (0, 1, 17)])
+    gs = orc.attention_bwd(*bits, "bf16", True, 0.2, qrows=sel, kcols=sel[::-1])
+    for r, (b, h, i) in enumerate(sel):
+        np.testing.assert_array_equal(gs["dq"][r], g["dq"][b, h, i])
+    for r, (b, h, j) in enumerate(sel[::-1]):
+        np.testing.assert_array_equal(gs["dk"][r], g["dk"][b, h, j])
+        np.testing.assert_array_equal(gs["dv"][r], g["dv"][b, h, j])
+
+
 PINS = [pin_widen_all_patterns, pin_worked_examples, pin_single_key, pin_causal_row0,
         pin_uniform_when_q_zero, pin_constant_v, pin_weights_sum_to_one, pin_split_combine,
         pin_permutation_invariance, pin_library_routine, pin_brute_force, pin_decode_gqa,
-        pin_widen_fp8, pin_fp8_library_routine, pin_fp8_single_key]
+        pin_widen_fp8, pin_fp8_library_routine, pin_fp8_single_key,
+        pin_bwd_finite_difference, pin_bwd_library_routine, pin_bwd_invariants,
+        pin_bwd_closed_forms, pin_bwd_forward_outputs]
 
 
 @pytest.fixture(scope="module")
@@ -363,6 +462,11 @@ MUTANTS = {
     12: "combine lse drops log of the weight sum",
     13: "E4M3 exponent bias 8",
     14: "value dequantization factor dropped",
+    15: "softmax Jacobian drops the row term sum_k P_ik dP_ik",
+    16: "dQ not multiplied by the scale",
+    17: "dV weights not normalised (lse dropped)",
+    18: "dK accumulates dO rows instead of q rows",
+    19: "dK/dV ignore the causal mask",
 }
 
 
