@@ -17,7 +17,10 @@ the two calls of every step give each call's average duration.
 
 After the timed steps, the FP8 forward (fa_fwd_fp8) is timed on the same
 forward shape with E4M3 inputs and reported in its own "fp8_fwd" object
-against the dense fp8 MFMA peak; it is not part of the step or of "value".
+against the dense fp8 MFMA peak, and the attention backward (fa_bwd: the dQ
+kernel, then the dK/dV kernel) on the same shape in its own "bwd" object
+(algorithmic FLOPs 2.5x the forward's: five N x N x d products).  Neither is
+part of the step or of "value".
 
 Prints ONE JSON line.
 """
@@ -148,6 +151,42 @@ def time_fp8(fa, synth, stream, steps, warmup):
             "source_digest": digest}
 
 
+def time_bwd(fa, synth, stream, steps, warmup):
+    """fa_bwd on the forward shape (o and lse from one fa_fwd): average call
+    time from HIP events on the launch stream."""
+    import torch
+    c = FWD
+    q, k, v, do = synth.bwd_inputs(c["B"], c["H"], c["N"], c["d"], c["dtype"], seed=c["seed"],
+                                   device=stream.device)
+    scale = 1 / math.sqrt(c["d"])
+    o, lse = fa.fwd(q, k, v, causal=c["causal"], scale=scale, stream=stream)
+    grads = [torch.empty_like(o) for _ in range(3)]
+    ws = torch.empty(fa.bwd_workspace_bytes(c["B"], c["H"], c["N"]), dtype=torch.uint8,
+                     device=stream.device)
+    kw = dict(causal=c["causal"], scale=scale, dq=grads[0], dk=grads[1], dv=grads[2],
+              workspace=ws, stream=stream)
+    for _ in range(warmup):
+        fa.bwd(q, k, v, o, lse, do, **kw)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fa.bwd(q, k, v, o, lse, do, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2.5 * fwd_flops(c["B"], c["H"], c["N"], c["d"], c["causal"])
+    tf = flops / (ms * 1e-3) / 1e12
+    digest = source_digest("fa_bwd.hip", "fa_device.hpp")
+    return {"kernels": "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel", "bound": "mfma",
+            "dtype": c["dtype"],
+            "workload": f"attention backward B{c['B']} H{c['H']} N{c['N']} d{c['d']} "
+                        f"{c['dtype']} non-causal",
+            "achieved": round(tf, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_MFMA_TFLOPS, 4), "avg_call_ms": round(ms, 4),
+            "algorithmic_flops_per_call": flops, "steps": steps, "source_digest": digest}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +195,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fp8-steps", type=int, default=50,
                     help="timed calls of the FP8 forward on the forward shape (0 skips it)")
+    ap.add_argument("--bwd-steps", type=int, default=20,
+                    help="timed fa_bwd calls for the bwd object (0: skip)")
     ap.add_argument("--only", choices=["fwd", "decode"], default=None,
                     help="time one call only (for profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -293,6 +334,8 @@ def main():
     }
     if args.fp8_steps > 0 and args.only is None:
         out["fp8_fwd"] = time_fp8(fa, synth, stream, args.fp8_steps, max(5, args.warmup // 2))
+    if args.bwd_steps > 0 and args.only is None:
+        out["bwd"] = time_bwd(fa, synth, stream, args.bwd_steps, 3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -46,6 +46,10 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_varlen.restype = I
         L.fa_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, F, F, F, F, P]
         L.fa_fwd_fp8.restype = I
+        L.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, I, P, S]
+        L.fa_bwd.restype = I
+        L.fa_bwd_workspace_bytes.argtypes = [I, I, I]
+        L.fa_bwd_workspace_bytes.restype = S
         L.fa_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, P, I]
         L.fa_decode.restype = I
         L.fa_decode_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, I, P, S]
@@ -178,6 +182,46 @@ def fwd_fp8(q, k, v, *, q_descale: float, k_descale: float, v_descale: float,
                           float(v_descale), _stream(stream, q.device))
     _check(st, "fa_fwd_fp8")
     return out, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(lib().fa_bwd_workspace_bytes(B, H, N))
+
+
+def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = None,
+        dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Attention backward.  q, k, v, dout: [B, H, N, d] bf16/fp16 CUDA
+    tensors (one dtype); o [B, H, N, d] and lse [B, H, N]: fp32 outputs of
+    ``fwd`` for the same q, k, v, causal and scale.  Returns
+    (dq, dk, dv), each [B, H, N, d] fp32."""
+    _need(q.dim() == 4 and q.shape == k.shape == v.shape == dout.shape,
+          "q, k, v, dout must share a [B,H,N,d] shape")
+    _need(q.dtype in _DTYPE and q.dtype == k.dtype == v.dtype == dout.dtype,
+          "q, k, v, dout must all be bf16 or all fp16")
+    B, H, N, d = q.shape
+    _need(o.shape == q.shape and o.dtype == torch.float32, "o must be fp32 [B,H,N,d]")
+    _need(lse.shape == (B, H, N) and lse.dtype == torch.float32, "lse must be fp32 [B,H,N]")
+    ts = (q, k, v, dout, o, lse)
+    _need(all(t.is_cuda and t.device == q.device for t in ts), "tensors must be on one GPU")
+    _need(all(t.is_contiguous() for t in ts), "tensors must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    outs = []
+    for g in (dq, dk, dv):
+        if g is None:
+            g = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+        _need(g.shape == q.shape and g.dtype == torch.float32 and g.is_contiguous()
+              and g.device == q.device, "gradients must be contiguous fp32 [B,H,N,d] tensors")
+        outs.append(g)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_bytes(B, H, N), 1), dtype=torch.uint8,
+                                device=q.device)
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(outs[0]),
+                      _ptr(outs[1]), _ptr(outs[2]), B, H, N, d, int(bool(causal)), float(scale),
+                      _stream(stream, q.device), _DTYPE[q.dtype], _ptr(workspace),
+                      workspace.numel() * workspace.element_size())
+    _check(st, "fa_bwd")
+    return tuple(outs)
 
 
 def decode_workspace_bytes(B: int, Hq: int, d: int, nsplit: int) -> int:

@@ -16,7 +16,7 @@ LIB = PKG / "libfa_amd.so"
 BUILD_DIR = ROOT / "_build"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_decode.hip"]
 # Per-source extra flags.  The forward kernel keeps its MFMA accumulators in
 # vector registers (the softmax reads S directly, O stays put); without this
 # the compiler parks them in accumulation registers and copies them back and

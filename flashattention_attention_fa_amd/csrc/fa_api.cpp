@@ -195,6 +195,58 @@ fa_status_t fa_fwd_fp8(const void *q, const void *k, const void *v, float *o, fl
     }
 }
 
+size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+    if (B < 0 || H < 0 || N < 0) return 0;
+    const unsigned long long rows = (unsigned long long)B * H * N;
+    if (rows > (1ull << 40)) return 0;
+    return 2 * round256((size_t)rows * sizeof(float));
+}
+
+fa_status_t fa_bwd(const void *q, const void *k, const void *v, const float *o, const void *dout,
+                   const float *lse, float *dq, float *dk, float *dv, int B, int H, int N, int d,
+                   int causal, float scale, hipStream_t stream, fa_dtype_t dtype, void *workspace,
+                   size_t workspace_bytes) {
+    try {
+        if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
+        if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+        if (!std::isfinite(scale)) return FA_ERR_VALUE;
+        if (B == 0 || H == 0 || N == 0) return FA_OK;
+        if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+        if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+            !aligned(dout, 16) || !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) ||
+            !aligned(dv, 16))
+            return FA_ERR_ALIGN;
+        const long long BH = (long long)B * H;
+        if (N > kMaxSeq || BH > INT_MAX || BH * ((N + 127) / 128) > INT_MAX) return FA_ERR_SHAPE;
+        const size_t need = fa_bwd_workspace_bytes(B, H, N);
+        if (need == 0) return FA_ERR_SHAPE;
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+            return FA_ERR_WORKSPACE;
+        fa::BwdArgs a;
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.dout = dout;
+        a.o = o;
+        a.lse = lse;
+        a.dq = dq;
+        a.dk = dk;
+        a.dv = dv;
+        a.ws_lse2 = static_cast<float *>(workspace);
+        a.ws_dl = reinterpret_cast<float *>(static_cast<char *>(workspace) + need / 2);
+        a.BH = (int)BH;
+        a.N = N;
+        a.d = d;
+        a.causal = causal != 0;
+        a.scale = scale;
+        a.dtype = dtype == FA_FP16 ? 1 : 0;
+        return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    } catch (...) {
+        return FA_ERR_INTERNAL;
+    }
+}
+
 size_t fa_decode_workspace_bytes(int B, int Hq, int d, int nsplit) {
     size_t o_bytes = 0, total = 0;
     if (d != 64 && d != 128) return 0;
@@ -314,7 +366,7 @@ const char *fa_status_string(fa_status_t status) {
         case FA_ERR_SHAPE: return "a size is negative, inconsistent or too large";
         case FA_ERR_UNSUPPORTED: return "unsupported head_dim (need 64 or 128) or dtype";
         case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-        case FA_ERR_WORKSPACE: return "decode workspace missing, misaligned or too small";
+        case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case FA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
         case FA_ERR_INTERNAL: return "internal error";
         case FA_ERR_VALUE: return "scale or a dequantization factor is not finite";
@@ -322,6 +374,6 @@ const char *fa_status_string(fa_status_t status) {
     return "unknown status";
 }
 
-int fa_version(void) { return 200; }
+int fa_version(void) { return 300; }
 
 }  // extern "C"

@@ -35,6 +35,20 @@ struct FwdFp8Args {
 
 hipError_t launch_fwd_fp8(const FwdFp8Args &a, hipStream_t stream);
 
+// Attention backward: gradients of the forward with upstream gradient dout.
+struct BwdArgs {
+    const void *q, *k, *v, *dout;   // [BH, N, d] 16-bit
+    const float *o, *lse;           // forward outputs: [BH, N, d], [BH, N]
+    float *dq, *dk, *dv;            // [BH, N, d]
+    float *ws_lse2, *ws_dl;         // workspace: [BH, N] each
+    int BH, N, d;
+    bool causal;
+    float scale;
+    int dtype;                      // 0 bf16, 1 fp16
+};
+
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
+
 struct DecodeArgs {
     const void *q;          // [B, Hq, d] 16-bit
     const void *k, *v;      // [B, Hkv, L, d] 16-bit

@@ -112,6 +112,41 @@ fa_status_t fa_fwd_fp8(const void *q, const void *k, const void *v, float *o,
                        float v_descale, hipStream_t stream);
 
 /*
+ * fa_bwd -- gradients of fa_fwd's attention (the attention backward, which
+ * "Warp Specialization in Triton: Design and Roadmap" lists on its roadmap
+ * as the next kernel after the forward).  For O = softmax(scale Q K^T
+ * [+ causal mask]) V and an upstream gradient dO = dL/dO, with
+ * P_ij = exp(scale <q_i, k_j> - lse_i) on the visible keys:
+ *     dV_j = sum_i P_ij dO_i
+ *     dS_ij = P_ij (<dO_i, v_j> - <dO_i, O_i>)
+ *     dQ_i = scale sum_j dS_ij k_j,    dK_j = scale sum_i dS_ij q_i
+ * o and lse are fa_fwd's outputs for the same q, k, v, causal and scale;
+ * P is rebuilt from lse, and nothing of size N x N is stored.  P and dS are
+ * rounded to the storage dtype for the products that consume them, with
+ * fp32 accumulation.  Two kernels run in stream order (dQ, then dK and dV);
+ * results are deterministic (no atomics).
+ *
+ *   q, k, v, dout : [B, H, N, d]  16-bit (dtype), device, 16-byte aligned
+ *   o             : [B, H, N, d]  fp32, device, 16-byte aligned
+ *   lse           : [B, H, N]     fp32, device (natural log, as fa_fwd writes)
+ *   dq, dk, dv    : [B, H, N, d]  fp32, device, 16-byte aligned (written)
+ *   d             : 64 or 128;  N <= 2^23
+ *   workspace     : device memory of at least fa_bwd_workspace_bytes(B, H, N)
+ *                   bytes, 256-byte aligned (FA_ERR_WORKSPACE otherwise);
+ *                   overwritten.  Calls sharing one workspace must not overlap.
+ * B == 0, H == 0 or N == 0 is a no-op returning FA_OK.
+ */
+fa_status_t fa_bwd(const void *q, const void *k, const void *v, const float *o,
+                   const void *dout, const float *lse, float *dq, float *dk,
+                   float *dv, int B, int H, int N, int d, int causal, float scale,
+                   hipStream_t stream, fa_dtype_t dtype, void *workspace,
+                   size_t workspace_bytes);
+
+/* Bytes of workspace fa_bwd needs: two fp32 values per query row, each array
+ * 256-byte aligned (0 for negative sizes). */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+
+/*
  * fa_decode -- attention of one new query token per sequence against a
  * key/value cache, split along the cache length into nsplit shards whose
  * partial results (O_s, lse_s) are combined by log-sum-exp reweighting

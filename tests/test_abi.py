@@ -19,7 +19,8 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = fa.declared_functions()
-    assert set(names) >= {"fa_fwd", "fa_fwd_varlen", "fa_fwd_fp8", "fa_decode", "fa_decode_ex", "fa_decode_paged",
+    assert set(names) >= {"fa_fwd", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd",
+                          "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_ex", "fa_decode_paged",
                           "fa_decode_workspace_bytes",
                           "fa_status_string", "fa_version"}
     for n in names:
@@ -52,6 +53,43 @@ def test_fwd_validation(L):
     assert fwd(L, scale=float("inf")) == VALUE
     assert fwd(L, N=(1 << 23) + 1) == SHAPE
     assert fwd(L, B=65536, H=65536) == SHAPE
+
+
+def bwd(L, q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A, B=1, H=2, N=100, d=64, causal=0,
+        scale=0.125, dtype=0, ws=0x100000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = L.fa_bwd_workspace_bytes(B, H, N)
+    return L.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, causal, scale, None, dtype, ws,
+                    ws_bytes)
+
+
+def test_bwd_validation(L):
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert bwd(L, **{name: None}) == NULL, name
+    for name in ("q", "k", "v", "o", "do", "dq", "dk", "dv"):
+        assert bwd(L, **{name: MIS}) == ALIGN, name
+    assert bwd(L, lse=A + 2) == ALIGN
+    assert bwd(L, B=-1) == SHAPE
+    assert bwd(L, N=-1) == SHAPE
+    assert bwd(L, d=96) == UNSUP
+    assert bwd(L, dtype=3) == UNSUP
+    assert bwd(L, scale=float("nan")) == VALUE
+    assert bwd(L, N=(1 << 23) + 1) == SHAPE
+    assert bwd(L, B=65536, H=65536) == SHAPE
+    assert bwd(L, ws=None) == WS
+    assert bwd(L, ws=0x100080) == WS
+    assert bwd(L, ws_bytes=L.fa_bwd_workspace_bytes(1, 2, 100) - 1) == WS
+    # empty problems return before any pointer is looked at
+    assert bwd(L, q=None, ws=None, B=0) == OK
+    assert bwd(L, q=None, ws=None, N=0) == OK
+
+
+def test_bwd_workspace_bytes(L):
+    # two fp32 arrays [B, H, N], each rounded up to 256 bytes
+    assert L.fa_bwd_workspace_bytes(2, 3, 100) == 2 * 2560
+    assert L.fa_bwd_workspace_bytes(1, 1, 1) == 512
+    assert L.fa_bwd_workspace_bytes(0, 3, 100) == 0
+    assert L.fa_bwd_workspace_bytes(-1, 3, 100) == 0
 
 
 def fwd8(L, q=A, k=A, v=A, o=A, lse=None, B=1, H=1, N=16, d=64, causal=0, scale=0.125,
