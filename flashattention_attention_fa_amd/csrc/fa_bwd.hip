@@ -285,10 +285,13 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(
 //   dS wave (role 1): holds V; dP = dO V^T; reads P; dS = P (dP - D);
 //                     dK^T += Q^T dS.
 // Each role keeps one operand and one accumulator in registers, so two waves
-// fit on a SIMD, and each does half of the tile's matrix products.  A tile
-// has two phases separated by a barrier: (S, softmax | dP) then
-// (dV | dS, dK); on each SIMD the partner's products run while a wave does
-// its exponentials or waits on LDS.
+// fit on a SIMD, and each does half of the tile's matrix products.  The two
+// roles run one query tile apart: in step j the P wave works on tile j and
+// the dS wave on tile j - 1, whose P the barrier ending step j - 1 published.
+// Nothing inside a step waits on the partner, so one wave's exponentials and
+// LDS waits hide under the other's products.  Query tiles, their statistics
+// and P rotate through three LDS buffers (tile j - 1 read by dS waves, tile j
+// by P waves, tile j + 1 being copied in).
 template <int D>
 struct BwdKvTile {
     static constexpr int WAVES = 8;
@@ -302,6 +305,7 @@ struct BwdKvTile {
     static constexpr int ROWS = BN / WAVES;
     static constexpr int LOADS = ROWS / RPI;
     static constexpr int ELEMS = BN * D;
+    static constexpr int PSLOTS = PAIRS * NB * 2 * 64;   // 16-byte P slots per buffer
     static constexpr int KSTEPS = D / 16;
     static constexpr int DB = D / 32;
     static_assert(ROWS % RPI == 0, "tile must split evenly over the waves");
@@ -318,11 +322,14 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
     typedef typename T::scalar scalar;
     constexpr int BN = C::BN, NB = C::NB, KSTEPS = C::KSTEPS, DB = C::DB;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Q0[C::ELEMS], Q1[C::ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t G0[C::ELEMS], G1[C::ELEMS];   // dO
-    __shared__ __attribute__((aligned(16))) float L0[BN], L1[BN], E0[BN], E1[BN];  // lse2, D
-    // P handed from each P wave to its partner: [pair][qb][u][lane], 16 bytes.
-    __shared__ __attribute__((aligned(16))) u32x4 Pl[C::PAIRS * NB * 2 * 64];
+    // Three rotating buffers of each kind, each its own LDS object so that
+    // every access names its buffer at compile time.
+    __shared__ __attribute__((aligned(16))) uint16_t Q0[C::ELEMS], Q1[C::ELEMS], Q2[C::ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t G0[C::ELEMS], G1[C::ELEMS], G2[C::ELEMS];
+    __shared__ __attribute__((aligned(16))) float L0[BN], L1[BN], L2[BN];   // lse2
+    __shared__ __attribute__((aligned(16))) float E0[BN], E1[BN], E2[BN];   // D
+    // P from each P wave to its partner: [pair][qb][u][lane], 16 bytes.
+    __shared__ __attribute__((aligned(16))) u32x4 P0[C::PSLOTS], P1[C::PSLOTS], P2[C::PSLOTS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -400,7 +407,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
         const uint16_t *p = buf + (32 * qb + 16 * u) * D;
         return join8<vec8>(lds_read_tr4(p + tcol[db]), lds_read_tr4(p + tcol8[db]));
     };
-    u32x4 *const pslot = Pl + pair * (NB * 2 * 64) + lane;   // + (2qb + u) * 64
+    const int pbase = pair * (NB * 2 * 64) + lane;   // slot (qb, u): pbase + (2qb + u) * 64
 
     // dV^T (P waves) or dK^T (dS waves): lane (li, lh), register r of block
     // db holds dim 32db + 8(r/4) + 4lh + r%4 of key my_k.
@@ -419,89 +426,103 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
 
     // S / dP blocks: lane (li, lh), register r holds query
     // 32qb + 8(r/4) + 4lh + r%4 against key my_k.
-    auto tile_step = [&](int j, const uint16_t *qbuf, const uint16_t *gbuf, const float *lbuf,
-                         const float *ebuf) __attribute__((always_inline)) {
-        if (role == 0) {
-            vec8 pb[NB][2];
-            const bool masked = j < mask_lo || j >= mask_hi;
+    auto p_work = [&](int j, const uint16_t *qbuf, const uint16_t *gbuf, const float *lbuf,
+                      u32x4 *pbuf) __attribute__((always_inline)) {
+        const bool masked = j < mask_lo || j >= mask_hi;
 #pragma unroll
-            for (int qb = 0; qb < NB; ++qb) {
-                floatx16 s;
+        for (int qb = 0; qb < NB; ++qb) {
+            floatx16 s;
 #pragma unroll
-                for (int t = 0; t < KSTEPS; ++t)
-                    s = T::mfma32(read_rows(qbuf, qb, t), kv[t], t == 0 ? zero16 : s);
+            for (int t = 0; t < KSTEPS; ++t)
+                s = T::mfma32(read_rows(qbuf, qb, t), kv[t], t == 0 ? zero16 : s);
+            vec8 pb[2];
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const floatx4 l4 = *(const floatx4 *)(lbuf + 32 * qb + 8 * a + 4 * lh);
+            for (int a = 0; a < 4; ++a) {
+                const floatx4 l4 = *(const floatx4 *)(lbuf + 32 * qb + 8 * a + 4 * lh);
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const int r = 4 * a + x;
-                        float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l4[x]));
-                        if (masked) {
-                            const int qi = j * BN + 32 * qb + 8 * a + 4 * lh + x;
-                            if (qi >= N || (CAUSAL && qi < my_k)) p = 0.f;
-                        }
-                        pb[qb][r >> 3][r & 7] = (scalar)p;
+                for (int x = 0; x < 4; ++x) {
+                    const int r = 4 * a + x;
+                    float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l4[x]));
+                    if (masked) {
+                        const int qi = j * BN + 32 * qb + 8 * a + 4 * lh + x;
+                        if (qi >= N || (CAUSAL && qi < my_k)) p = 0.f;
                     }
+                    pb[r >> 3][r & 7] = (scalar)p;
                 }
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-                    pslot[(2 * qb + u) * 64] = __builtin_bit_cast(u32x4, pb[qb][u]);
             }
-            __syncthreads();
 #pragma unroll
-            for (int qb = 0; qb < NB; ++qb)
+            for (int u = 0; u < 2; ++u) {
+                pbuf[pbase + (2 * qb + u) * 64] = __builtin_bit_cast(u32x4, pb[u]);
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
+                for (int db = 0; db < DB; ++db)
+                    acc[db] = T::mfma32(read_tr(gbuf, qb, u, db), pb[u], acc[db]);
+            }
+        }
+    };
+    auto ds_work = [&](const uint16_t *qbuf, const uint16_t *gbuf, const float *ebuf,
+                       const u32x4 *pbuf) __attribute__((always_inline)) {
 #pragma unroll
-                    for (int db = 0; db < DB; ++db)
-                        acc[db] = T::mfma32(read_tr(gbuf, qb, u, db), pb[qb][u], acc[db]);
-        } else {
-            floatx16 dp[NB];
+        for (int qb = 0; qb < NB; ++qb) {
+            floatx16 dp;
 #pragma unroll
-            for (int qb = 0; qb < NB; ++qb)
+            for (int t = 0; t < KSTEPS; ++t)
+                dp = T::mfma32(read_rows(gbuf, qb, t), kv[t], t == 0 ? zero16 : dp);
 #pragma unroll
-                for (int t = 0; t < KSTEPS; ++t)
-                    dp[qb] = T::mfma32(read_rows(gbuf, qb, t), kv[t], t == 0 ? zero16 : dp[qb]);
-            __syncthreads();
+            for (int u = 0; u < 2; ++u) {
+                const vec8 pv = __builtin_bit_cast(vec8, pbuf[pbase + (2 * qb + u) * 64]);
+                const floatx4 e0 = *(const floatx4 *)(ebuf + 32 * qb + 16 * u + 4 * lh);
+                const floatx4 e1 = *(const floatx4 *)(ebuf + 32 * qb + 16 * u + 8 + 4 * lh);
+                vec8 dsb;
 #pragma unroll
-            for (int qb = 0; qb < NB; ++qb) {
-                vec8 dsb[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const vec8 pv = __builtin_bit_cast(vec8, pslot[(2 * qb + u) * 64]);
-                    const floatx4 e0 = *(const floatx4 *)(ebuf + 32 * qb + 16 * u + 4 * lh);
-                    const floatx4 e1 = *(const floatx4 *)(ebuf + 32 * qb + 16 * u + 8 + 4 * lh);
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) {
-                        const float e = x < 4 ? e0[x] : e1[x - 4];
-                        dsb[u][x] = (scalar)((float)pv[x] * (dp[qb][8 * u + x] - e));
-                    }
+                for (int x = 0; x < 8; ++x) {
+                    const float e = x < 4 ? e0[x] : e1[x - 4];
+                    dsb[x] = (scalar)((float)pv[x] * (dp[8 * u + x] - e));
                 }
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-                        acc[db] = T::mfma32(read_tr(qbuf, qb, u, db), dsb[u], acc[db]);
+                for (int db = 0; db < DB; ++db)
+                    acc[db] = T::mfma32(read_tr(qbuf, qb, u, db), dsb, acc[db]);
             }
         }
     };
 
-    if (qt0 < nqt) load_tile(qt0, Q0, G0, L0, E0);
+    // Step j: copy tile j + 1, P waves on tile j, dS waves on tile j - 1.
+    // Buffer set b holds tiles j with (j - qt0) % 3 == b.
+    auto step = [&](int j, auto par) __attribute__((always_inline)) {
+        constexpr int B = decltype(par)::value;
+        uint16_t *const qc = B == 0 ? Q0 : B == 1 ? Q1 : Q2;   // tile j
+        uint16_t *const gc = B == 0 ? G0 : B == 1 ? G1 : G2;
+        float *const lc = B == 0 ? L0 : B == 1 ? L1 : L2;
+        u32x4 *const pc = B == 0 ? P0 : B == 1 ? P1 : P2;
+        uint16_t *const qp = B == 0 ? Q2 : B == 1 ? Q0 : Q1;   // tile j - 1
+        uint16_t *const gp = B == 0 ? G2 : B == 1 ? G0 : G1;
+        float *const ep = B == 0 ? E2 : B == 1 ? E0 : E1;
+        u32x4 *const pp = B == 0 ? P2 : B == 1 ? P0 : P1;
+        uint16_t *const qn = B == 0 ? Q1 : B == 1 ? Q2 : Q0;   // tile j + 1
+        uint16_t *const gn = B == 0 ? G1 : B == 1 ? G2 : G0;
+        float *const ln = B == 0 ? L1 : B == 1 ? L2 : L0;
+        float *const en = B == 0 ? E1 : B == 1 ? E2 : E0;
+        if (j + 1 < nqt) load_tile(j + 1, qn, gn, ln, en);
+        if (role == 0) {
+            if (j < nqt) p_work(j, qc, gc, lc, pc);
+        } else {
+            if (j > qt0) ds_work(qp, gp, ep, pp);
+        }
+        wait_vmem();
+        __syncthreads();
+    };
+
+    load_tile(qt0, Q0, G0, L0, E0);
     wait_vmem();
     __syncthreads();
-    int j = qt0;
-    for (; j + 1 < nqt; j += 2) {
-        load_tile(j + 1, Q1, G1, L1, E1);
-        tile_step(j, Q0, G0, L0, E0);
-        wait_vmem();
-        __syncthreads();
-        if (j + 2 < nqt) load_tile(j + 2, Q0, G0, L0, E0);
-        tile_step(j + 1, Q1, G1, L1, E1);
-        wait_vmem();
-        __syncthreads();
+    typedef std::integral_constant<int, 0> S0;
+    typedef std::integral_constant<int, 1> S1;
+    typedef std::integral_constant<int, 2> S2;
+    // nqt - qt0 + 1 steps: the dS waves finish one step after the P waves.
+    for (int j = qt0; j <= nqt; j += 3) {
+        step(j, S0{});
+        if (j + 1 <= nqt) step(j + 1, S1{});
+        if (j + 2 <= nqt) step(j + 2, S2{});
     }
-    if (j < nqt) tile_step(j, Q0, G0, L0, E0);
 
     if (my_k < N) {
         float *row = (role ? dk : dv) + head + (size_t)my_k * D + 4 * lh;
