@@ -184,7 +184,10 @@ def time_bwd(fa, synth, stream, steps, warmup):
                         f"{c['dtype']} non-causal",
             "achieved": round(tf, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / PEAK_MFMA_TFLOPS, 4), "avg_call_ms": round(ms, 4),
-            "algorithmic_flops_per_call": flops, "steps": steps, "source_digest": digest}
+            "algorithmic_flops_per_call": flops, "steps": steps,
+            "traffic": {kern: load_traffic(kern, digest)
+                        for kern in ("fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel")},
+            "source_digest": digest}
 
 
 def main():
