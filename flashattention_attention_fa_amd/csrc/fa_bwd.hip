@@ -409,6 +409,38 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
     };
     const int pbase = pair * (NB * 2 * 64) + lane;   // slot (qb, u): pbase + (2qb + u) * 64
 
+    // Scheduling patterns for the matrix-product phases: keep several LDS
+    // operand reads in flight ahead of the products that consume them (left
+    // to itself the scheduler issues one read, waits, then multiplies).
+    // Measured on MI355X: 5 % faster without the mask, 3-5 % slower with
+    // it, so only the unmasked kernel uses them.
+    constexpr bool kSched = !CAUSAL;
+    auto fence = [&]() __attribute__((always_inline)) {
+        if constexpr (kSched) __builtin_amdgcn_sched_barrier(0);
+    };
+    auto sched_chain = [&]() __attribute__((always_inline)) {   // KSTEPS reads, KSTEPS MFMAs
+        if constexpr (kSched) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // LDS reads
+#pragma unroll
+            for (int i = 0; i < KSTEPS - 3; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        }
+    };
+    auto sched_tr = [&]() __attribute__((always_inline)) {      // 4*DB reads, 2*DB MFMAs
+        if constexpr (kSched) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * DB - 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+    };
+
     // dV^T (P waves) or dK^T (dS waves): lane (li, lh), register r of block
     // db holds dim 32db + 8(r/4) + 4lh + r%4 of key my_k.
     floatx16 acc[DB];
@@ -432,9 +464,12 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
 #pragma unroll
         for (int qb = 0; qb < NB; ++qb) {
             floatx16 s;
+            fence();
 #pragma unroll
             for (int t = 0; t < KSTEPS; ++t)
                 s = T::mfma32(read_rows(qbuf, qb, t), kv[t], t == 0 ? zero16 : s);
+            sched_chain();
+            fence();
             vec8 pb[2];
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
@@ -450,6 +485,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
                     pb[r >> 3][r & 7] = (scalar)p;
                 }
             }
+            fence();
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 pbuf[pbase + (2 * qb + u) * 64] = __builtin_bit_cast(u32x4, pb[u]);
@@ -457,6 +493,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
                 for (int db = 0; db < DB; ++db)
                     acc[db] = T::mfma32(read_tr(gbuf, qb, u, db), pb[u], acc[db]);
             }
+            sched_tr();
+            fence();
         }
     };
     auto ds_work = [&](const uint16_t *qbuf, const uint16_t *gbuf, const float *ebuf,
@@ -464,24 +502,32 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
 #pragma unroll
         for (int qb = 0; qb < NB; ++qb) {
             floatx16 dp;
+            fence();
 #pragma unroll
             for (int t = 0; t < KSTEPS; ++t)
                 dp = T::mfma32(read_rows(gbuf, qb, t), kv[t], t == 0 ? zero16 : dp);
+            sched_chain();
+            fence();
+            vec8 dsb[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const vec8 pv = __builtin_bit_cast(vec8, pbuf[pbase + (2 * qb + u) * 64]);
                 const floatx4 e0 = *(const floatx4 *)(ebuf + 32 * qb + 16 * u + 4 * lh);
                 const floatx4 e1 = *(const floatx4 *)(ebuf + 32 * qb + 16 * u + 8 + 4 * lh);
-                vec8 dsb;
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
                     const float e = x < 4 ? e0[x] : e1[x - 4];
-                    dsb[x] = (scalar)((float)pv[x] * (dp[8 * u + x] - e));
+                    dsb[u][x] = (scalar)((float)pv[x] * (dp[8 * u + x] - e));
                 }
+            }
+            fence();
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
-                    acc[db] = T::mfma32(read_tr(qbuf, qb, u, db), dsb, acc[db]);
-            }
+                    acc[db] = T::mfma32(read_tr(qbuf, qb, u, db), dsb[u], acc[db]);
+            sched_tr();
+            fence();
         }
     };
 
