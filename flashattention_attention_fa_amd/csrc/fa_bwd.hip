@@ -20,11 +20,13 @@
 //                      then dQ^T += K^T dS^T with K^T from the transposing
 //                      LDS read.  First it computes D_i from dO and O and
 //                      writes D and lse*log2(e) to the workspace.
-//  fa_bwd_dkdv_kernel  each wave owns 32 keys (K, V in registers); Q, dO and
-//                      the per-query lse and D of 64 queries stream through
-//                      LDS.  Per tile: S = Q K^T and dP = dO V^T, then
-//                      dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T
-//                      from transposing LDS reads.
+//  fa_bwd_dkdv_kernel  each pair of waves owns 32 keys; Q, dO and the
+//                      per-query lse and D of 64 queries stream through LDS.
+//                      One wave of the pair holds K: S = Q K^T, P, and
+//                      dV^T += dO^T P; the other holds V: dP = dO V^T,
+//                      dS = P (dP - D) with P handed over through LDS, and
+//                      dK^T += Q^T dS.  dO^T and Q^T come from transposing
+//                      LDS reads.
 // The dQ kernel must run first (the second reads its D and lse).  S and dP
 // are formed in both kernels: 7 matrix products per tile pair instead of the
 // 5 of a single pass that accumulates dQ with atomics.

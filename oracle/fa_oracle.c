@@ -377,10 +377,12 @@ static double elem_at(const void *p, long idx, int dtype)
 }
 
 /* Per-row statistics of one head: lse_i and Dl_i = sum_k P_ik dP_ik, plus
- * O_i when o is not NULL.  Rows run in parallel. */
+ * O_i when o is not NULL, for the rows with want[i] != 0 (every row when
+ * want is NULL).  Rows run in parallel. */
 static int head_row_stats(const double *q, const double *k, const double *v,
                           const double *dout, long N, long d, int causal,
-                          double scale, double *lse, double *dl, double *o)
+                          double scale, const char *want, double *lse,
+                          double *dl, double *o)
 {
     int bad = 0;
 #pragma omp parallel
@@ -393,7 +395,7 @@ static int head_row_stats(const double *q, const double *k, const double *v,
         }
 #pragma omp for schedule(dynamic, 4)
         for (long i = 0; i < N; ++i) {
-            if (!s || !oi)
+            if (!s || !oi || (want && !want[i]))
                 continue;
             double m = -INFINITY;
             for (long j = 0; j < N; ++j) {
@@ -503,7 +505,24 @@ int oracle_attention_bwd(const void *q, const void *k, const void *v,
             hv[e] = elem_at(v, base + (long)e, dtype);
             hdo[e] = elem_at(dout, base + (long)e, dtype);
         }
-        if (head_row_stats(hq, hk, hv, hdo, N, d, causal, scale, lse, dl, ho)) {
+        /* dK and dV need every row's statistics; dQ rows only their own. */
+        int all_rows = 0;
+        for (long r = 0; r < nk && !all_rows; ++r)
+            all_rows = kcols[3 * r] == b && kcols[3 * r + 1] == h;
+        char *want = NULL;
+        if (!all_rows) {
+            want = (char *)calloc((size_t)(N ? N : 1), 1);
+            if (!want) {
+                rc = -1;
+                break;
+            }
+            for (long r = 0; r < nq; ++r)
+                if (qrows[3 * r] == b && qrows[3 * r + 1] == h)
+                    want[qrows[3 * r + 2]] = 1;
+        }
+        int st = head_row_stats(hq, hk, hv, hdo, N, d, causal, scale, want, lse, dl, ho);
+        free(want);
+        if (st) {
             rc = -1;
             break;
         }

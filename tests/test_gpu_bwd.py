@@ -140,6 +140,36 @@ def test_bench_shape_causal_sampled(orc):
     run_sampled(orc, 8, 32, 8192, 128, "bf16", True, seed=2301, heads=[(0, 0), (5, 9)])
 
 
+def test_long_single_head_causal(orc):
+    """One causal head of 2^21 tokens (512 MiB per 16-bit tensor): 32-bit
+    buffer offsets near their range.  dQ on sampled rows against the oracle;
+    dK and dV through properties that hold at any size."""
+    B, H, N, d = 1, 1, 1 << 21, 128
+    print(f"case bwd long causal B{B} H{H} N{N} d{d} bf16", flush=True)
+    q, k, v, do = synth.bwd_inputs(B, H, N, d, "bf16", seed=2600, device=DEV)
+    scale = 1 / math.sqrt(d)
+    dq, dk, dv = gpu_grads(q, k, v, do, True, scale)
+    rows = [0, 1, 63, 64, 127, 128, 4095, 4096, N // 2, N - 129, N - 128, N - 2, N - 1]
+    sel = np.array([(0, 0, i) for i in rows], np.int64)
+    got = dq[0, 0, torch.as_tensor(rows)].cpu().numpy()
+    sdv = dv.double().sum(dim=2)
+    sdo = do.double().sum(dim=2)
+    err_v = ((sdv - sdo).norm() / sdo.norm()).item()
+    err_k = (dk.double().sum(dim=2).norm() /
+             (dk.double().pow(2).mean().sqrt() * math.sqrt(N) * math.sqrt(d))).item()
+    print(f"long causal: sum dV vs sum dO rel {err_v:.2e}; |sum dK| / (sqrt(N) rms) {err_k:.2e}",
+          flush=True)
+    assert err_v < 5e-3 and err_k < 2e-2
+    assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
+    bits = [synth.to_bits(t) for t in (q, k, v, do)]
+    del q, k, v, do, dq, dk, dv
+    torch.cuda.empty_cache()
+    ref = orc.attention_bwd(*bits, "bf16", True, scale, qrows=sel, kcols=np.zeros((0, 3)))
+    bound = GRAD_MAX_ABS_REL * float(np.abs(ref["dq"]).max())
+    assert_close(got, ref["dq"], what="bwd long causal dq rows", o_max_abs=bound,
+                 o_rel_l2=GRAD_REL_L2)
+
+
 def test_deterministic(orc):
     """No atomics: two runs give bitwise identical gradients."""
     print("case bwd determinism B2 H4 N1000 d128 bf16 causal", flush=True)

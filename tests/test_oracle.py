@@ -409,6 +409,11 @@ def pin_bwd_forward_outputs(orc):
     for r, (b, h, j) in enumerate(sel[::-1]):
         np.testing.assert_array_equal(gs["dk"][r], g["dk"][b, h, j])
         np.testing.assert_array_equal(gs["dv"][r], g["dv"][b, h, j])
+    # dQ rows alone (no key columns): only those rows' statistics are formed.
+    gq = orc.attention_bwd(*bits, "bf16", True, 0.2, qrows=sel, kcols=np.zeros((0, 3)))
+    for r, (b, h, i) in enumerate(sel):
+        np.testing.assert_array_equal(gq["dq"][r], g["dq"][b, h, i])
+        np.testing.assert_array_equal(gq["lse"][r], g["lse"][b, h, i])
 
 
 PINS = [pin_widen_all_patterns, pin_worked_examples, pin_single_key, pin_causal_row0,
