@@ -1,7 +1,8 @@
 /*
- * fa.h -- C ABI of libfa_amd.so: exact attention forward (FlashAttention
- * tiling, online softmax, log-sum-exp) and split-KV flash-decode for AMD
- * Instinct MI355X (gfx950).
+ * fa.h -- C ABI of libfa_amd.so for AMD Instinct MI355X (gfx950): exact
+ * attention forward (FlashAttention tiling, online softmax, log-sum-exp) on
+ * 16-bit and FP8 inputs and on packed variable-length batches; its backward
+ * (dQ, dK, dV); and split-KV flash-decode over dense or paged caches.
  *
  * Plain pointers and sizes only.  Every tensor pointer is a DEVICE pointer
  * owned by the caller; the library keeps none of them after a call returns
