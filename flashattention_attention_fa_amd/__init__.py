@@ -48,6 +48,9 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_fp8.restype = I
         L.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, I, P, S]
         L.fa_bwd.restype = I
+        L.fa_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, I, P,
+                                    S]
+        L.fa_bwd_varlen.restype = I
         L.fa_bwd_workspace_bytes.argtypes = [I, I, I]
         L.fa_bwd_workspace_bytes.restype = S
         L.fa_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, P, I]
@@ -221,6 +224,46 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = No
                       _stream(stream, q.device), _DTYPE[q.dtype], _ptr(workspace),
                       workspace.numel() * workspace.element_size())
     _check(st, "fa_bwd")
+    return tuple(outs)
+
+
+def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, *, causal: bool = False,
+               scale: float | None = None, dq=None, dk=None, dv=None, workspace=None,
+               stream=None):
+    """Backward of ``fwd_varlen``.  q, k, v, dout: packed [T, H, d] bf16/fp16;
+    o [T, H, d] and lse [H, T] fp32 from ``fwd_varlen``; cu_seqlens: int32
+    [B + 1] on the device.  Returns (dq, dk, dv), each [T, H, d] fp32 (rows
+    outside every sequence are left as allocated)."""
+    _need(q.dim() == 3 and q.shape == k.shape == v.shape == dout.shape,
+          "q, k, v, dout must share a [T,H,d] shape")
+    _need(q.dtype in _DTYPE and q.dtype == k.dtype == v.dtype == dout.dtype,
+          "q, k, v, dout must all be bf16 or all fp16")
+    T, H, d = q.shape
+    _need(o.shape == q.shape and o.dtype == torch.float32, "o must be fp32 [T,H,d]")
+    _need(lse.shape == (H, T) and lse.dtype == torch.float32, "lse must be fp32 [H,T]")
+    _need(cu_seqlens.dim() == 1 and cu_seqlens.dtype == torch.int32, "cu_seqlens: int32 [B+1]")
+    ts = (q, k, v, dout, o, lse, cu_seqlens)
+    _need(all(t.is_cuda and t.device == q.device for t in ts), "tensors must be on one GPU")
+    _need(all(t.is_contiguous() for t in ts), "tensors must be contiguous")
+    B = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    outs = []
+    for g in (dq, dk, dv):
+        if g is None:
+            g = torch.empty((T, H, d), dtype=torch.float32, device=q.device)
+        _need(g.shape == q.shape and g.dtype == torch.float32 and g.is_contiguous()
+              and g.device == q.device, "gradients must be contiguous fp32 [T,H,d] tensors")
+        outs.append(g)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_bytes(1, H, T), 1), dtype=torch.uint8,
+                                device=q.device)
+    st = lib().fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                             _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(cu_seqlens), B, H,
+                             T, int(max_seqlen), d, int(bool(causal)), float(scale),
+                             _stream(stream, q.device), _DTYPE[q.dtype], _ptr(workspace),
+                             workspace.numel() * workspace.element_size())
+    _check(st, "fa_bwd_varlen")
     return tuple(outs)
 
 

@@ -247,6 +247,58 @@ fa_status_t fa_bwd(const void *q, const void *k, const void *v, const float *o, 
     }
 }
 
+fa_status_t fa_bwd_varlen(const void *q, const void *k, const void *v, const float *o,
+                          const void *dout, const float *lse, float *dq, float *dk, float *dv,
+                          const int *cu_seqlens, int B, int H, int total_tokens, int max_seqlen,
+                          int d, int causal, float scale, hipStream_t stream, fa_dtype_t dtype,
+                          void *workspace, size_t workspace_bytes) {
+    try {
+        if (B < 0 || H < 0 || total_tokens < 0 || max_seqlen < 0 || d < 0) return FA_ERR_SHAPE;
+        if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+        if (!std::isfinite(scale)) return FA_ERR_VALUE;
+        if (B == 0 || H == 0 || total_tokens == 0 || max_seqlen == 0) return FA_OK;
+        if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens)
+            return FA_ERR_NULL;
+        if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+            !aligned(dout, 16) || !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) ||
+            !aligned(dv, 16) || !aligned(cu_seqlens, 4))
+            return FA_ERR_ALIGN;
+        const long long BH = (long long)B * H;
+        if ((long long)max_seqlen * H * d >= (1ll << 30) || BH > INT_MAX ||
+            BH * ((max_seqlen + 127) / 128) > INT_MAX)
+            return FA_ERR_SHAPE;
+        const size_t need = fa_bwd_workspace_bytes(1, H, total_tokens);
+        if (need == 0) return FA_ERR_SHAPE;
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+            return FA_ERR_WORKSPACE;
+        fa::BwdArgs a;
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.dout = dout;
+        a.o = o;
+        a.lse = lse;
+        a.dq = dq;
+        a.dk = dk;
+        a.dv = dv;
+        a.ws_lse2 = static_cast<float *>(workspace);
+        a.ws_dl = reinterpret_cast<float *>(static_cast<char *>(workspace) + need / 2);
+        a.BH = (int)BH;
+        a.N = max_seqlen;
+        a.d = d;
+        a.causal = causal != 0;
+        a.scale = scale;
+        a.dtype = dtype == FA_FP16 ? 1 : 0;
+        a.cu_seqlens = cu_seqlens;
+        a.H = H;
+        a.T = total_tokens;
+        return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    } catch (...) {
+        return FA_ERR_INTERNAL;
+    }
+}
+
 size_t fa_decode_workspace_bytes(int B, int Hq, int d, int nsplit) {
     size_t o_bytes = 0, total = 0;
     if (d != 64 && d != 128) return 0;

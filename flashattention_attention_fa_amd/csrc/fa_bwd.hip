@@ -84,16 +84,53 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc_at(const void *head_
     return make_rsrc((const void *)(uintptr_t)(((uint64_t)hi << 32) | lo), n);
 }
 
+// Packed variable-length batches (VARLEN): q, k, v, dO, o and the gradients
+// are [T, H, D] with sequence b at rows [cu[b], cu[b+1]); lse and the
+// workspace statistics are [H, T].
+struct BwdSeqs {
+    const int *cu;   // [B + 1]
+    int H, T;
+};
+
+// One (sequence, head) as a kernel sees it: N rows starting at element
+// `head`, consecutive rows RS elements apart, statistics of row i at
+// srow0 + i.  Varlen bounds read from cu are clamped to [0, T] and to Nmax.
+// Consecutive (sequence, head) pairs of the grid are ordered head-major
+// across sequences, so that each XCD's contiguous range of workgroups holds
+// an equal share of every sequence.
+template <int D, bool VARLEN>
+struct BwdHead {
+    int bh, N;
+    size_t head, srow0;
+    static constexpr int rs(const BwdSeqs &vl) { return VARLEN ? vl.H * D : D; }
+    __device__ BwdHead(int pair_id, int npairs, int Nmax, const BwdSeqs &vl) {
+        bh = pair_id;
+        N = Nmax;
+        head = (size_t)bh * Nmax * D;
+        srow0 = (size_t)bh * Nmax;
+        if constexpr (VARLEN) {
+            const int nseq = npairs / vl.H;
+            bh = (pair_id % nseq) * vl.H + pair_id / nseq;
+            const int b = bh / vl.H, h = bh % vl.H;
+            const int s0 = min(max(vl.cu[b], 0), vl.T);
+            const int e = min(max(vl.cu[b + 1], s0), vl.T);
+            N = min(e - s0, Nmax);
+            head = ((size_t)s0 * vl.H + h) * D;
+            srow0 = (size_t)h * vl.T + s0;
+        }
+    }
+};
+
 // ---------------------------------------------------------------------------
 // dQ (and D, lse2) kernel
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ o,
     const uint16_t *__restrict__ dout, const float *__restrict__ lse,
-    float *__restrict__ dq, float *__restrict__ ws_lse2, float *__restrict__ ws_dl, int N,
-    int nq, float c, float scale) {
+    float *__restrict__ dq, float *__restrict__ ws_lse2, float *__restrict__ ws_dl, int Nmax,
+    int nq, float c, float scale, BwdSeqs vl) {
     typedef BwdTile<D> C;
     typedef typename T::vec8 vec8;
     typedef typename T::scalar scalar;
@@ -110,11 +147,14 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(
     // Block -> (head, q-tile): consecutive ids walk one head's q-tiles (they
     // share its K and V in the XCD's L2); causal: longest rows first.
     const unsigned id = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = (int)(id / (unsigned)nq);
     const int qt = CAUSAL ? nq - 1 - (int)(id % (unsigned)nq) : (int)(id % (unsigned)nq);
     const int q0 = qt * C::BM;
-    const size_t head = (size_t)bh * N * D;
-    const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
+    const BwdHead<D, VARLEN> hd((int)(id / (unsigned)nq), (int)(gridDim.x / (unsigned)nq), Nmax, vl);
+    const int N = hd.N;
+    const size_t head = hd.head;
+    const int RS = BwdHead<D, VARLEN>::rs(vl);
+    if (VARLEN && q0 >= N) return;   // past this sequence: leave before any barrier
+    const uint32_t head_bytes = (uint32_t)((N > 0 ? (size_t)(N - 1) * RS + D : 0) * 2);
     const int my_q = q0 + wave * 32 + li;
     const bool q_ok = my_q < N;
 
@@ -126,13 +166,13 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(
     float dl = 0.f;
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
-        const uint32_t off = (uint32_t)(my_q * D + 16 * t + 8 * lh) * 2u;
+        const uint32_t off = (uint32_t)(my_q * RS + 16 * t + 8 * lh) * 2u;
         qf[t] = as_vec8<vec8>(buffer_load16(qr, off));
         df[t] = as_vec8<vec8>(buffer_load16(dr, off));
     }
     // D_i = <dO_i, O_i> with dO as stored (16 bit) and O in fp32.
     if (q_ok) {
-        const float *orow = o + head + (size_t)my_q * D + 8 * lh;
+        const float *orow = o + head + (size_t)my_q * RS + 8 * lh;
 #pragma unroll
         for (int t = 0; t < KSTEPS; ++t) {
             const floatx4 a = *(const floatx4 *)(orow + 16 * t);
@@ -145,10 +185,10 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(
         }
     }
     dl = sum_halves(dl);
-    const float lse2 = q_ok ? lse[(size_t)bh * N + my_q] * kLog2e : 0.f;
+    const float lse2 = q_ok ? lse[hd.srow0 + my_q] * kLog2e : 0.f;
     if (q_ok && lh == 0) {
-        ws_lse2[(size_t)bh * N + my_q] = lse2;
-        ws_dl[(size_t)bh * N + my_q] = dl;
+        ws_lse2[hd.srow0 + my_q] = lse2;
+        ws_dl[hd.srow0 + my_q] = dl;
     }
 
     const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
@@ -161,11 +201,11 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(
     for (int i = 0; i < C::LOADS; ++i) {
         const int row = wave * C::ROWS + i * C::RPI + lane / C::KCH;
         const int pos = lane % C::KCH;
-        koff[i] = (uint32_t)(row * D + 8 * (pos ^ swz_kt<D>(row))) * 2u;
-        voff[i] = (uint32_t)(row * D + 8 * (pos ^ swz_kt<D>(row))) * 2u;
+        koff[i] = (uint32_t)(row * RS + 8 * (pos ^ swz_kt<D>(row))) * 2u;
+        voff[i] = (uint32_t)(row * RS + 8 * (pos ^ swz_kt<D>(row))) * 2u;
     }
     auto load_tile = [&](int tile, uint16_t *kbuf, uint16_t *vbuf) __attribute__((always_inline)) {
-        const uint32_t off = (uint32_t)tile * (uint32_t)(BN * D * 2);
+        const uint32_t off = (uint32_t)tile * (uint32_t)(BN * RS * 2);
         const __amdgpu_buffer_rsrc_t rk = tile_rsrc_at(k + head, off, head_bytes);
         const __amdgpu_buffer_rsrc_t rv = tile_rsrc_at(v + head, off, head_bytes);
 #pragma unroll
@@ -266,7 +306,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(
     // dQ^T accumulator: lane (li, lh), register r of block db holds dim
     // 32db + 8(r/4) + 4lh + r%4 of query my_q.
     if (q_ok) {
-        float *row = dq + head + (size_t)my_q * D + 4 * lh;
+        float *row = dq + head + (size_t)my_q * RS + 4 * lh;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -313,12 +353,13 @@ struct BwdKvTile {
     static_assert(ROWS % RPI == 0, "tile must split evenly over the waves");
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
     const float *__restrict__ ws_lse2, const float *__restrict__ ws_dl,
-    float *__restrict__ dk, float *__restrict__ dv, int N, int nk, float c, float scale) {
+    float *__restrict__ dk, float *__restrict__ dv, int Nmax, int nk, float c, float scale,
+    BwdSeqs vl) {
     typedef BwdKvTile<D> C;
     typedef typename T::vec8 vec8;
     typedef typename T::scalar scalar;
@@ -343,11 +384,14 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
     // (sharing its Q and dO in L2); causal: the first key tiles see the most
     // queries, so ascending order runs the longest first.
     const unsigned id = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = (int)(id / (unsigned)nk);
     const int kt = (int)(id % (unsigned)nk);
     const int k0 = kt * C::BM;
-    const size_t head = (size_t)bh * N * D;
-    const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
+    const BwdHead<D, VARLEN> hd((int)(id / (unsigned)nk), (int)(gridDim.x / (unsigned)nk), Nmax, vl);
+    const int N = hd.N;
+    const size_t head = hd.head;
+    const int RS = BwdHead<D, VARLEN>::rs(vl);
+    if (VARLEN && k0 >= N) return;   // past this sequence: leave before any barrier
+    const uint32_t head_bytes = (uint32_t)((N > 0 ? (size_t)(N - 1) * RS + D : 0) * 2);
     const uint32_t stat_bytes = (uint32_t)((size_t)N * 4);
     const int my_k = k0 + 32 * pair + li;
 
@@ -357,7 +401,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
     vec8 kv[KSTEPS];
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t)
-        kv[t] = as_vec8<vec8>(buffer_load16(kr, (uint32_t)(my_k * D + 16 * t + 8 * lh) * 2u));
+        kv[t] = as_vec8<vec8>(buffer_load16(kr, (uint32_t)(my_k * RS + 16 * t + 8 * lh) * 2u));
 
     // Query tiles [qt0, nqt): causal skips the tiles wholly before k0.
     const int qt0 = CAUSAL ? k0 / BN : 0;
@@ -367,13 +411,13 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
         const int row = wave * C::ROWS + i * C::RPI + lane / C::KCH;
-        toff[i] = (uint32_t)(row * D + 8 * ((lane % C::KCH) ^ swz_kt<D>(row))) * 2u;
+        toff[i] = (uint32_t)(row * RS + 8 * ((lane % C::KCH) ^ swz_kt<D>(row))) * 2u;
     }
     // Waves 0 and 1 also copy the tile's lse2 and D (one dword per lane;
     // past N reads as zero and is masked).
     auto load_tile = [&](int tile, uint16_t *qbuf, uint16_t *gbuf, float *lbuf, float *ebuf)
                          __attribute__((always_inline)) {
-        const uint32_t off = (uint32_t)tile * (uint32_t)(BN * D * 2);
+        const uint32_t off = (uint32_t)tile * (uint32_t)(BN * RS * 2);
         const __amdgpu_buffer_rsrc_t rq = tile_rsrc_at(q + head, off, head_bytes);
         const __amdgpu_buffer_rsrc_t rg = tile_rsrc_at(dout + head, off, head_bytes);
 #pragma unroll
@@ -384,7 +428,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
         if (wave < 2) {
             const uint32_t soff = (uint32_t)tile * (uint32_t)(BN * 4);
             const float *src = wave == 0 ? ws_lse2 : ws_dl;
-            const __amdgpu_buffer_rsrc_t rs = tile_rsrc_at(src + (size_t)bh * N, soff, stat_bytes);
+            const __amdgpu_buffer_rsrc_t rs = tile_rsrc_at(src + hd.srow0, soff, stat_bytes);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rs, (__attribute__((address_space(3))) void *)(wave == 0 ? lbuf : ebuf), 4,
                 (int)(lane * 4), 0, 0, 0);
@@ -510,26 +554,39 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
                 dp = T::mfma32(read_rows(gbuf, qb, t), kv[t], t == 0 ? zero16 : dp);
             sched_chain();
             fence();
-            vec8 dsb[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            auto make_ds = [&](int u) __attribute__((always_inline)) {
                 const vec8 pv = __builtin_bit_cast(vec8, pbuf[pbase + (2 * qb + u) * 64]);
                 const floatx4 e0 = *(const floatx4 *)(ebuf + 32 * qb + 16 * u + 4 * lh);
                 const floatx4 e1 = *(const floatx4 *)(ebuf + 32 * qb + 16 * u + 8 + 4 * lh);
+                vec8 ds;
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
                     const float e = x < 4 ? e0[x] : e1[x - 4];
-                    dsb[u][x] = (scalar)((float)pv[x] * (dp[8 * u + x] - e));
+                    ds[x] = (scalar)((float)pv[x] * (dp[8 * u + x] - e));
+                }
+                return ds;
+            };
+            if constexpr (kSched) {
+                // Both halves first, then one scheduled product phase.
+                const vec8 dsb[2] = {make_ds(0), make_ds(1)};
+                fence();
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        acc[db] = T::mfma32(read_tr(qbuf, qb, u, db), dsb[u], acc[db]);
+                sched_tr();
+                fence();
+            } else {
+                // Half by half (fewer live registers).
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const vec8 dsb = make_ds(u);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        acc[db] = T::mfma32(read_tr(qbuf, qb, u, db), dsb, acc[db]);
                 }
             }
-            fence();
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    acc[db] = T::mfma32(read_tr(qbuf, qb, u, db), dsb[u], acc[db]);
-            sched_tr();
-            fence();
         }
     };
 
@@ -573,7 +630,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
     }
 
     if (my_k < N) {
-        float *row = (role ? dk : dv) + head + (size_t)my_k * D + 4 * lh;
+        float *row = (role ? dk : dv) + head + (size_t)my_k * RS + 4 * lh;
         const float f = role ? scale : 1.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -585,6 +642,27 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
     }
 }
 
+template <typename T, int D, bool CAUSAL, bool VARLEN>
+static hipError_t launch_kernels(const BwdArgs &a, int nt, unsigned blocks, int ntk,
+                                 unsigned blocks_k, hipStream_t stream) {
+    typedef BwdTile<D> C;
+    typedef BwdKvTile<D> CK;
+    const float c = a.scale * kLog2e;
+    const BwdSeqs vl = {a.cu_seqlens, a.H, a.T};
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL, VARLEN>), dim3(blocks), dim3(C::THREADS), 0,
+                       stream, (const uint16_t *)a.q, (const uint16_t *)a.k,
+                       (const uint16_t *)a.v, a.o, (const uint16_t *)a.dout, a.lse, a.dq,
+                       a.ws_lse2, a.ws_dl, a.N, nt, c, a.scale, vl);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>), dim3(blocks_k),
+                       dim3(CK::THREADS), 0, stream, (const uint16_t *)a.q,
+                       (const uint16_t *)a.k, (const uint16_t *)a.v,
+                       (const uint16_t *)a.dout, a.ws_lse2, a.ws_dl, a.dk, a.dv, a.N, ntk, c,
+                       a.scale, vl);
+    return hipGetLastError();
+}
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch(const BwdArgs &a, hipStream_t stream) {
     typedef BwdTile<D> C;
@@ -594,20 +672,12 @@ static hipError_t launch(const BwdArgs &a, hipStream_t stream) {
     const int ntk = (a.N + CK::BM - 1) / CK::BM;
     const long long blocks_k = (long long)ntk * a.BH;
     if (blocks > 0x7fffffffLL || blocks_k > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const float c = a.scale * kLog2e;
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)blocks),
-                       dim3(C::THREADS), 0, stream, (const uint16_t *)a.q,
-                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.o,
-                       (const uint16_t *)a.dout, a.lse, a.dq, a.ws_lse2, a.ws_dl, a.N, nt, c,
-                       a.scale);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)blocks_k),
-                       dim3(CK::THREADS), 0, stream, (const uint16_t *)a.q,
-                       (const uint16_t *)a.k, (const uint16_t *)a.v,
-                       (const uint16_t *)a.dout, a.ws_lse2, a.ws_dl, a.dk, a.dv, a.N, ntk, c,
-                       a.scale);
-    return hipGetLastError();
+    // N = the longest sequence when varlen; BH = B * H.
+    if (a.cu_seqlens != nullptr)
+        return launch_kernels<T, D, CAUSAL, true>(a, nt, (unsigned)blocks, ntk,
+                                                  (unsigned)blocks_k, stream);
+    return launch_kernels<T, D, CAUSAL, false>(a, nt, (unsigned)blocks, ntk, (unsigned)blocks_k,
+                                               stream);
 }
 
 template <typename T>

@@ -45,6 +45,11 @@ struct BwdArgs {
     bool causal;
     float scale;
     int dtype;                      // 0 bf16, 1 fp16
+    // Packed variable-length batch (cu_seqlens != nullptr): tensors are
+    // [T, H, d], BH = B*H, N = the longest sequence, lse and the workspace
+    // arrays are [H, T].
+    const int *cu_seqlens = nullptr;   // [B + 1]
+    int H = 0, T = 0;
 };
 
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);

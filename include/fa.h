@@ -148,6 +148,34 @@ fa_status_t fa_bwd(const void *q, const void *k, const void *v, const float *o,
 size_t fa_bwd_workspace_bytes(int B, int H, int N);
 
 /*
+ * fa_bwd_varlen -- fa_bwd for a packed variable-length batch, the backward of
+ * fa_fwd_varlen (same layout and bounds): sequence b occupies rows
+ * [cu_seqlens[b], cu_seqlens[b+1]) of tensors shaped [total_tokens, H, d],
+ * and each sequence attends only to itself.
+ *
+ *   q, k, v, dout : [total_tokens, H, d]  16-bit (dtype), device, 16-byte aligned
+ *   o             : [total_tokens, H, d]  fp32 (fa_fwd_varlen's output)
+ *   lse           : [H, total_tokens]     fp32 (fa_fwd_varlen's output)
+ *   dq, dk, dv    : [total_tokens, H, d]  fp32 (written; rows that belong to
+ *                   no sequence are left untouched)
+ *   cu_seqlens    : [B + 1] int32, device, non-decreasing, cu_seqlens[B] <=
+ *                   total_tokens (bounds are clamped to [0, total_tokens]);
+ *                   max_seqlen >= the longest sequence (longer ones are cut
+ *                   to max_seqlen, as in fa_fwd_varlen)
+ *   d             : 64 or 128;  max_seqlen * H * d < 2^30
+ *   workspace     : at least fa_bwd_workspace_bytes(1, H, total_tokens) bytes,
+ *                   256-byte aligned (FA_ERR_WORKSPACE otherwise)
+ * B, H, total_tokens or max_seqlen == 0 is a no-op returning FA_OK.
+ */
+fa_status_t fa_bwd_varlen(const void *q, const void *k, const void *v,
+                          const float *o, const void *dout, const float *lse,
+                          float *dq, float *dk, float *dv, const int *cu_seqlens,
+                          int B, int H, int total_tokens, int max_seqlen, int d,
+                          int causal, float scale, hipStream_t stream,
+                          fa_dtype_t dtype, void *workspace,
+                          size_t workspace_bytes);
+
+/*
  * fa_decode -- attention of one new query token per sequence against a
  * key/value cache, split along the cache length into nsplit shards whose
  * partial results (O_s, lse_s) are combined by log-sum-exp reweighting

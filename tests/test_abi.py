@@ -19,7 +19,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = fa.declared_functions()
-    assert set(names) >= {"fa_fwd", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd",
+    assert set(names) >= {"fa_fwd", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd", "fa_bwd_varlen",
                           "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_ex", "fa_decode_paged",
                           "fa_decode_workspace_bytes",
                           "fa_status_string", "fa_version"}
@@ -82,6 +82,32 @@ def test_bwd_validation(L):
     # empty problems return before any pointer is looked at
     assert bwd(L, q=None, ws=None, B=0) == OK
     assert bwd(L, q=None, ws=None, N=0) == OK
+
+
+def bwdv(L, q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A, cu=A, B=2, H=2, T=100, maxs=60,
+         d=64, causal=0, scale=0.125, dtype=0, ws=0x100000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = L.fa_bwd_workspace_bytes(1, H, T)
+    return L.fa_bwd_varlen(q, k, v, o, do, lse, dq, dk, dv, cu, B, H, T, maxs, d, causal, scale,
+                           None, dtype, ws, ws_bytes)
+
+
+def test_bwd_varlen_validation(L):
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "cu"):
+        assert bwdv(L, **{name: None}) == NULL, name
+    for name in ("q", "k", "v", "o", "do", "dq", "dk", "dv"):
+        assert bwdv(L, **{name: MIS}) == ALIGN, name
+    assert bwdv(L, cu=A + 2) == ALIGN
+    assert bwdv(L, B=-1) == SHAPE
+    assert bwdv(L, maxs=-1) == SHAPE
+    assert bwdv(L, d=80) == UNSUP
+    assert bwdv(L, dtype=5) == UNSUP
+    assert bwdv(L, scale=float("inf")) == VALUE
+    assert bwdv(L, maxs=1 << 22, H=4) == SHAPE
+    assert bwdv(L, ws=None) == WS
+    assert bwdv(L, ws_bytes=L.fa_bwd_workspace_bytes(1, 2, 100) - 1) == WS
+    assert bwdv(L, q=None, cu=None, ws=None, B=0) == OK
+    assert bwdv(L, q=None, cu=None, ws=None, T=0) == OK
 
 
 def test_bwd_workspace_bytes(L):
