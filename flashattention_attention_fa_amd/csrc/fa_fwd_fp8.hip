@@ -89,13 +89,21 @@ struct Fp8Tile {
     static_assert(INSTR % COPY_WAVES == 0, "copies must split evenly over the waves");
 };
 
-// Chunk c of row r is stored at chunk position c ^ swz(r): 16 consecutive
-// rows read at one logical chunk (K) and 8 consecutive rows read at one
-// chunk (V, transposing read) land in distinct bank slots.
+// Chunk c of row r is stored at chunk position c ^ swz(r), with g = r / RPL
+// (the row's bank line) and Q = KCH / 2 aligned chunk pairs per row:
+//   swz(r) = 2 (g mod Q) + (g div Q) mod 2.
+// K (16-byte reads, 16 consecutive rows at one logical chunk): over 2Q
+// consecutive lines swz takes every value once, so the rows land in
+// distinct bank slots.  V (transposing byte reads, 8 consecutive rows at the
+// two chunks of one aligned pair): rows in different lines get different
+// pairs (swz / 2 differs), so the 8 rows x 2 chunks fill distinct slots.
+// (The plainer (g mod KCH) maps both chunks of a pair onto one pair for
+// neighbouring lines: a 2-way conflict on every V read, measured 1 % slower.)
 template <int D>
 __device__ __forceinline__ int swz8(int r) {
-    constexpr int KCH = D / 16, RPL = 16 / KCH;
-    return (r / RPL) % KCH;
+    constexpr int KCH = D / 16, RPL = 16 / KCH, Q = KCH / 2;
+    const int g = r / RPL;
+    return 2 * (g % Q) + (g / Q) % 2;
 }
 
 template <int D, bool CAUSAL>
