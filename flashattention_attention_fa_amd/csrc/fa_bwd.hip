@@ -592,8 +592,9 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
 
     // Step j: copy tile j + 1, P waves on tile j, dS waves on tile j - 1.
     // Buffer set b holds tiles j with (j - qt0) % 3 == b.
-    auto step = [&](int j, auto par) __attribute__((always_inline)) {
+    auto step = [&](int j, auto par, auto role_tag) __attribute__((always_inline)) {
         constexpr int B = decltype(par)::value;
+        constexpr int ROLE = decltype(role_tag)::value;
         uint16_t *const qc = B == 0 ? Q0 : B == 1 ? Q1 : Q2;   // tile j
         uint16_t *const gc = B == 0 ? G0 : B == 1 ? G1 : G2;
         float *const lc = B == 0 ? L0 : B == 1 ? L1 : L2;
@@ -607,7 +608,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
         float *const ln = B == 0 ? L1 : B == 1 ? L2 : L0;
         float *const en = B == 0 ? E1 : B == 1 ? E2 : E0;
         if (j + 1 < nqt) load_tile(j + 1, qn, gn, ln, en);
-        if (role == 0) {
+        if constexpr (ROLE == 0) {
             if (j < nqt) p_work(j, qc, gc, lc, pc);
         } else {
             if (j > qt0) ds_work(qp, gp, ep, pp);
@@ -623,11 +624,19 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
     typedef std::integral_constant<int, 1> S1;
     typedef std::integral_constant<int, 2> S2;
     // nqt - qt0 + 1 steps: the dS waves finish one step after the P waves.
-    for (int j = qt0; j <= nqt; j += 3) {
-        step(j, S0{});
-        if (j + 1 <= nqt) step(j + 1, S1{});
-        if (j + 2 <= nqt) step(j + 2, S2{});
-    }
+    // One loop per role (the role is uniform in each wave), so each keeps its
+    // accumulator in one place; both loops pass the same barriers.
+    auto run = [&](auto role_tag) __attribute__((always_inline)) {
+        for (int j = qt0; j <= nqt; j += 3) {
+            step(j, S0{}, role_tag);
+            if (j + 1 <= nqt) step(j + 1, S1{}, role_tag);
+            if (j + 2 <= nqt) step(j + 2, S2{}, role_tag);
+        }
+    };
+    if (role == 0)
+        run(std::integral_constant<int, 0>{});
+    else
+        run(std::integral_constant<int, 1>{});
 
     if (my_k < N) {
         float *row = (role ? dk : dv) + head + (size_t)my_k * RS + 4 * lh;
