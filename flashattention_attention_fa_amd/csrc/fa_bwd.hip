@@ -253,8 +253,10 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(
     if (CAUSAL) n_full = min(n_full, q0 / BN);
     const int lim = CAUSAL ? min(N - 1, my_q) : N - 1;
 
-    auto tile_step = [&](int j, const uint16_t *kbuf, const uint16_t *vbuf)
+    // MASK is a compile-time tag: tiles without masked keys carry no mask code.
+    auto tile_step = [&](int j, const uint16_t *kbuf, const uint16_t *vbuf, auto mask_tag)
                          __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         vec8 dsb[NB][2];
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb) {
@@ -266,11 +268,10 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(
                 s = T::mfma32(read_rows(kbuf, kb, t), qf[t], t == 0 ? zero16 : s);
                 dp = T::mfma32(read_rows(vbuf, kb, t), df[t], t == 0 ? zero16 : dp);
             }
-            const bool masked = j >= n_full;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-                if (masked) {
+                if constexpr (MASK) {
                     const int key = j * BN + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
                     if (key > lim) p = 0.f;
                 }
@@ -287,21 +288,31 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(
     };
 
     // Tile j sits in buffer j % 2; tile j+1 is copied while j is computed.
+    typedef std::integral_constant<int, 0> B0;
+    typedef std::integral_constant<int, 1> B1;
+    auto iter = [&](int j, auto par, auto mask_tag) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par)::value;
+        if (j + 1 < ntiles) load_tile(j + 1, PAR ? K0 : K1, PAR ? V0 : V1);
+        tile_step(j, PAR ? K1 : K0, PAR ? V1 : V0, mask_tag);
+        wait_vmem();
+        __syncthreads();
+    };
+    // Tiles [j0, j1), unrolled by two so that buffer parities are static.
+    auto run = [&](int j0, int j1, auto mask_tag) __attribute__((always_inline)) {
+        int j = j0;
+        if (j < j1 && (j & 1)) iter(j++, B1{}, mask_tag);
+        for (; j + 1 < j1; j += 2) {
+            iter(j, B0{}, mask_tag);
+            iter(j + 1, B1{}, mask_tag);
+        }
+        if (j < j1) iter(j, B0{}, mask_tag);
+    };
     if (ntiles > 0) load_tile(0, K0, V0);
     wait_vmem();
     __syncthreads();
-    int j = 0;
-    for (; j + 1 < ntiles; j += 2) {
-        load_tile(j + 1, K1, V1);
-        tile_step(j, K0, V0);
-        wait_vmem();
-        __syncthreads();
-        if (j + 2 < ntiles) load_tile(j + 2, K0, V0);
-        tile_step(j + 1, K1, V1);
-        wait_vmem();
-        __syncthreads();
-    }
-    if (j < ntiles) tile_step(j, K0, V0);
+    const int split = max(0, min(n_full, ntiles));
+    run(0, split, std::false_type{});
+    run(split, ntiles, std::true_type{});
 
     // dQ^T accumulator: lane (li, lh), register r of block db holds dim
     // 32db + 8(r/4) + 4lh + r%4 of query my_q.
@@ -505,8 +516,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
     // S / dP blocks: lane (li, lh), register r holds query
     // 32qb + 8(r/4) + 4lh + r%4 against key my_k.
     auto p_work = [&](int j, const uint16_t *qbuf, const uint16_t *gbuf, const float *lbuf,
-                      u32x4 *pbuf) __attribute__((always_inline)) {
-        const bool masked = j < mask_lo || j >= mask_hi;
+                      u32x4 *pbuf, auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
         for (int qb = 0; qb < NB; ++qb) {
             floatx16 s;
@@ -524,7 +535,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
                 for (int x = 0; x < 4; ++x) {
                     const int r = 4 * a + x;
                     float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l4[x]));
-                    if (masked) {
+                    if constexpr (MASK) {
                         const int qi = j * BN + 32 * qb + 8 * a + 4 * lh + x;
                         if (qi >= N || (CAUSAL && qi < my_k)) p = 0.f;
                     }
@@ -592,7 +603,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
 
     // Step j: copy tile j + 1, P waves on tile j, dS waves on tile j - 1.
     // Buffer set b holds tiles j with (j - qt0) % 3 == b.
-    auto step = [&](int j, auto par, auto role_tag) __attribute__((always_inline)) {
+    auto step = [&](int j, auto par, auto role_tag, auto mask_tag) __attribute__((always_inline)) {
         constexpr int B = decltype(par)::value;
         constexpr int ROLE = decltype(role_tag)::value;
         uint16_t *const qc = B == 0 ? Q0 : B == 1 ? Q1 : Q2;   // tile j
@@ -609,7 +620,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
         float *const en = B == 0 ? E1 : B == 1 ? E2 : E0;
         if (j + 1 < nqt) load_tile(j + 1, qn, gn, ln, en);
         if constexpr (ROLE == 0) {
-            if (j < nqt) p_work(j, qc, gc, lc, pc);
+            if (j < nqt) p_work(j, qc, gc, lc, pc, mask_tag);
         } else {
             if (j > qt0) ds_work(qp, gp, ep, pp);
         }
@@ -626,12 +637,26 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
     // nqt - qt0 + 1 steps: the dS waves finish one step after the P waves.
     // One loop per role (the role is uniform in each wave), so each keeps its
     // accumulator in one place; both loops pass the same barriers.
-    auto run = [&](auto role_tag) __attribute__((always_inline)) {
-        for (int j = qt0; j <= nqt; j += 3) {
-            step(j, S0{}, role_tag);
-            if (j + 1 <= nqt) step(j + 1, S1{}, role_tag);
-            if (j + 2 <= nqt) step(j + 2, S2{}, role_tag);
+    // Steps [j0, j1) with a static buffer phase (j - qt0) % 3; the P waves'
+    // tiles in [mask_lo, mask_hi) need no mask and run without mask code.
+    auto range = [&](int j0, int j1, auto role_tag, auto mask_tag) __attribute__((always_inline)) {
+        int j = j0;
+        if (j < j1 && (j - qt0) % 3 == 1) step(j++, S1{}, role_tag, mask_tag);
+        if (j < j1 && (j - qt0) % 3 == 2) step(j++, S2{}, role_tag, mask_tag);
+        for (; j + 2 < j1; j += 3) {
+            step(j, S0{}, role_tag, mask_tag);
+            step(j + 1, S1{}, role_tag, mask_tag);
+            step(j + 2, S2{}, role_tag, mask_tag);
         }
+        if (j < j1) step(j++, S0{}, role_tag, mask_tag);
+        if (j < j1) step(j++, S1{}, role_tag, mask_tag);
+    };
+    const int lo = max(qt0, min(mask_lo, nqt + 1));
+    const int hi = max(lo, min(mask_hi, nqt + 1));
+    auto run = [&](auto role_tag) __attribute__((always_inline)) {
+        range(qt0, lo, role_tag, std::true_type{});
+        range(lo, hi, role_tag, std::false_type{});
+        range(hi, nqt + 1, role_tag, std::true_type{});
     };
     if (role == 0)
         run(std::integral_constant<int, 0>{});
