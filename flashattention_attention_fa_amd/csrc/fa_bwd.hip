@@ -573,7 +573,9 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
                     const float e = x < 4 ? e0[x] : e1[x - 4];
-                    ds[x] = (scalar)((float)pv[x] * (dp[8 * u + x] - e));
+                    // Written as an FMA with a zero addend (same rounding as the
+                    // product) so that fp16 P is widened inside v_fma_mix_f32.
+                    ds[x] = (scalar)__builtin_fmaf((float)pv[x], dp[8 * u + x] - e, 0.f);
                 }
                 return ds;
             };
