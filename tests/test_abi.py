@@ -244,3 +244,19 @@ def test_python_binding_rejects_bad_tensors():
         fa.fwd(q, q, q)
     with pytest.raises(ValueError):
         fa.decode(q[:, :, 0], q, q.half(), nsplit=2)
+    o = torch.zeros(1, 2, 8, 64)
+    lse = torch.zeros(1, 2, 8)
+    with pytest.raises(ValueError):      # o must be fp32
+        fa.bwd(q, q, q, o.half(), lse, q)
+    with pytest.raises(ValueError):      # lse shape
+        fa.bwd(q, q, q, o, lse[:, :1], q)
+    with pytest.raises(ValueError):      # dout dtype differs
+        fa.bwd(q, q, q, o, lse, q.half())
+    with pytest.raises(ValueError):      # CPU tensors
+        fa.bwd(q, q, q, o, lse, q)
+    p = torch.zeros(16, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 16], dtype=torch.int32)
+    with pytest.raises(ValueError):      # lse must be [H, T]
+        fa.bwd_varlen(p, p, p, torch.zeros(16, 2, 64), torch.zeros(16, 2), p, cu, 16)
+    with pytest.raises(ValueError):      # cu_seqlens must be int32
+        fa.bwd_varlen(p, p, p, torch.zeros(16, 2, 64), torch.zeros(2, 16), p, cu.long(), 16)
