@@ -32,9 +32,11 @@
 //    subnormals.  l sums the fp32 p' (the scale cancels in O = sum p'v / l;
 //    lse subtracts it).  E4M3's largest value is 448 = 2^8.8, so every p'
 //    must stay at or below it: the running max m is taken exactly from the
-//    first tile, and a later tile whose lane sums of p' pass 448 has its
-//    exact row maximum checked; if some score exceeds m + 2.8 (log2 units),
-//    m is raised to it (O and l rescaled) and the tile recomputed.
+//    first tile.  Each lane tracks the largest score of its tile next to the
+//    exponentials; if one exceeds m + 2.8 (log2 units, i.e. p' could pass
+//    448), m is raised to the tile's row maximum (O and l rescaled) and the
+//    tile recomputed.  (A cheaper-looking test on the lane sums of p' fires
+//    on almost every tile: 32 weights of up to 64 often sum past 448.)
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -65,11 +67,9 @@ __device__ __forceinline__ int cvt_fp8x4(float a, float b, float c2, float d) {
     return __builtin_amdgcn_cvt_pk_fp8_f32(c2, d, lo, true);
 }
 
-// Largest finite E4M3 value, and the weight scale 2^kPShift.
-constexpr float kFp8Max = 448.0f;
+// The weight scale 2^kPShift.  m is raised when a score passes m + kRaise
+// (log2 units): 2^(kRaise + kPShift) stays below 448, E4M3's largest value.
 constexpr float kPShift = 6.0f;
-// m is raised when a score passes m + kRaise (log2 units): 2^(kRaise+kPShift)
-// stays below 448.
 constexpr float kRaise = 2.8f;
 
 template <int D, bool CAUSAL>
@@ -262,9 +262,9 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_fp8
     // P^T operand bytes: dword w = 4kb + (r/4) of pb holds registers
     // 4(w%4) .. +3 of block kb.
     i32x8 pb;
-    float tsum = 0.f;
+    float tsum = 0.f, xmax = 0.f;
     auto softmax_part = [&](const floatx16 (&x)[KB], int kb, int half) __attribute__((always_inline)) {
-        if (kb == 0 && half == 0) tsum = 0.f;
+        if (kb == 0 && half == 0) { tsum = 0.f; xmax = x[0][0]; }
         const float bias = kPShift - m_run;
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
@@ -274,23 +274,20 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_fp8
             for (int e = 0; e < 4; ++e) {
                 p[e] = __builtin_amdgcn_exp2f(fmaf(x[kb][r0 + e], c, bias));
                 tsum += p[e];
+                xmax = __builtin_elementwise_maximum(xmax, x[kb][r0 + e]);
             }
             pb[4 * kb + r0 / 4] = cvt_fp8x4(p[0], p[1], p[2], p[3]);
         }
     };
-    // Accept the tile's weights; rare path: if some p' might pass the E4M3
-    // range, check the exact row maximum and raise m when needed.
     auto accept = [&](const floatx16 (&x)[KB]) __attribute__((always_inline)) {
-        if (__any(!(tsum <= kFp8Max))) {
+        if (__any(!(xmax * c <= m_run + kRaise))) {
             asm volatile("" ::: "memory");
             row_max(x);
-            if (__any(mt > m_run + kRaise)) {
-                raise_max();
+            raise_max();
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) softmax_part(x, kb, h);
-            }
+                for (int h = 0; h < 2; ++h) softmax_part(x, kb, h);
         }
         l_run += tsum;
     };
