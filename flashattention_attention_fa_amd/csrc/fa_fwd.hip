@@ -18,7 +18,8 @@
 // The loop is also software pipelined inside each wave (the pages contrast
 // this "different iterations of one role" schedule with warp
 // specialisation): iteration j issues the QK^T MFMAs of tile j+1 next to the
-// exponentials of tile j, then the PV MFMAs of tile j.
+// exponentials of tile j, then the PV MFMAs of tile j next to the exponents
+// (c*s - m) of tile j+1, so that both MFMA phases carry vector work.
 //
 // Per wave and tile (32 queries x 64 keys):
 //   S^T = K Q^T   MFMA 32x32x16; Q lives in registers for the whole loop
@@ -68,24 +69,23 @@ struct FwdTile {
     static_assert(ROWS % RPI == 0, "tile must split evenly over the waves");
 };
 
-// LDS tiles are unpadded (direct copies write 1 KB contiguous per wave
-// instruction); bank conflicts are avoided by permuting the 16-byte chunks of
-// each row.  Chunk c of row r is stored at chunk position c ^ swz(r).
-//  K tile, read 16 bytes per lane with 32 consecutive rows per instruction:
-//    swz = (r / ROWS_PER_LINE) % KCH spreads 16 consecutive rows over all 16
-//    chunk positions of a bank line.
-//  V tile, read by the transposing read (4 rows x 32 bytes per 16 lanes):
-//    swz = 4 * ((r / ROWS_PER_LINE) % (KCH / 4)) gives the 4 rows of a group
-//    disjoint chunk quadruples.
+// LDS tiles are unpadded: a direct copy writes 1 KB contiguous per wave
+// instruction, 16 bytes per lane, each lane from any global address.
+//  K tile, row-major, read 16 bytes per lane with 32 consecutive rows per
+//    instruction.  Chunk c of row r is stored at chunk position c ^ swz_k(r);
+//    swz_k = (r / ROWS_PER_LINE) % KCH spreads 16 consecutive rows over all
+//    16 chunk positions of a bank line.
+//  V tile, in 64-byte slabs: slab (q, r) holds dims 32q..32q+31 of key row r,
+//    at element (q * BN + r) * 32.  The transposing read takes 4 consecutive
+//    rows x 32 bytes per 16 lanes, 4 rows x 64 bytes per half wave: four
+//    consecutive slabs, i.e. 256 bytes on distinct banks.  Every read address
+//    is one per-lane register plus a compile-time offset (dim block, key
+//    block), where a row-major tile with a row swizzle needs one register
+//    per dim block.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
     constexpr int KCH = D / 8, ROWS_PER_LINE = 16 / KCH;
     return (r / ROWS_PER_LINE) % KCH;
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int r) {
-    constexpr int KCH = D / 8, ROWS_PER_LINE = 16 / KCH;
-    return 4 * ((r / ROWS_PER_LINE) % (KCH / 4));
 }
 
 // Bound on one lane's sum of the unnormalised weights of a tile.  The running
@@ -185,19 +185,25 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_ker
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int ntiles = (kv_end + BN - 1) / BN;
 
-    // Tile copies go straight from global memory into LDS.  Wave w copies
-    // rows [w*ROWS, (w+1)*ROWS) of a tile, RPI rows per instruction; lane l
+    // Tile copies go straight from global memory into LDS.  Copy
+    // instruction n = wave*LOADS + i of a tile fills elements
+    // [512n, 512n + 512) of its buffer.  K: rows [RPI*n, RPI*(n+1)); lane l
     // fills chunk position l%KCH of its row with the source chunk that the
-    // swizzle puts there.  Rows past N read as zero (buffer range check) and
+    // swizzle puts there.  V: slabs [16n, 16n + 16); lane l fills a quarter
+    // of slab 16n + l/4.  Rows past N read as zero (buffer range check) and
     // are masked out of the softmax; tiles past the last one are copied the
     // same way and never read.
+    static_assert(C::RPI * D == 512, "one copy instruction fills 512 elements");
     uint32_t koff[C::LOADS], voff[C::LOADS];
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-        const int row = wave * C::ROWS + i * C::RPI + lane / KCH;
+        const int n = wave * C::LOADS + i;
+        const int row = n * C::RPI + lane / KCH;
         const int pos = lane % KCH;
         koff[i] = (uint32_t)(row * RS + 8 * (pos ^ swz_k<D>(row))) * 2u;
-        voff[i] = (uint32_t)(row * RS + 8 * (pos ^ swz_v<D>(row))) * 2u;
+        const int slab = 16 * n + lane / 4;
+        const int vq = slab / BN, vrow = slab % BN;
+        voff[i] = (uint32_t)(vrow * RS + 32 * vq + 8 * (lane % 4)) * 2u;
     }
     // The tile's base goes into the (scalar) buffer resource, so the
     // per-lane offsets stay fixed and the range check still covers the end of
@@ -215,13 +221,13 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_ker
         const __amdgpu_buffer_rsrc_t r = tile_rsrc(k + head, tile);
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
-            buffer_load16_lds(r, koff[i], buf + (wave * C::ROWS + i * C::RPI) * D);
+            buffer_load16_lds(r, koff[i], buf + 512 * (wave * C::LOADS + i));
     };
     auto load_v = [&](int tile, uint16_t *buf) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t r = tile_rsrc(v + head, tile);
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
-            buffer_load16_lds(r, voff[i], buf + (wave * C::ROWS + i * C::RPI) * D);
+            buffer_load16_lds(r, voff[i], buf + 512 * (wave * C::LOADS + i));
     };
 
     // K operand of block kb, step t: logical chunk 2t + lh of row 32kb + li.
@@ -233,18 +239,12 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_ker
     };
     // V^T operand of PV MFMA (kb, u, db) by two transposing reads: lane j of
     // each 16-lane group points at row 32kb + 16u + 4lh + j/4 (+8 for the
-    // second read) and logical column 32db + 16*(group&1) + 4*(j%4).  The
-    // row swizzle is the same for all those rows.
-    const int tr_row = 4 * lh + ((lane & 15) >> 2);
-    int vcol[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        vcol[db] = tr_row * D + 8 * ((col >> 3) ^ swz_v<D>(tr_row)) + (col & 7);
-    }
+    // second read) and dim 32db + 16*(group&1) + 4*(j%4), i.e. slab
+    // (db, row), element 16*(group&1) + 4*(j%4).
+    const int vlane = (4 * lh + ((lane & 15) >> 2)) * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     auto read_v = [&](const uint16_t *buf, int kb, int u, int db) __attribute__((always_inline)) {
-        const uint16_t *p = buf + (32 * kb + 16 * u) * D + vcol[db];
-        return join8<vec8>(lds_read_tr4(p), lds_read_tr4(p + 8 * D));
+        const uint16_t *p = buf + (db * BN + 32 * kb + 16 * u) * 32 + vlane;
+        return join8<vec8>(lds_read_tr4(p), lds_read_tr4(p + 8 * 32));
     };
 
     floatx16 oacc[DB];
@@ -301,30 +301,55 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_ker
     // pb[kb][r/8]; PV MFMA (kb, u) contracts over keys
     // 32kb + 16u + 8(e/4) + 4lh + e%4.
     vec8 pb[KB][2];
-    // m is finite from tile 0 on (every query sees key 0), so the softmax
-    // needs no guard against an infinite base.  tsum collects this lane's
-    // part of the tile's row sum, from the fp32 weights (the 16-bit rounding
-    // of P, up to 2^-9 relative for bf16, stays out of l and lse).
+    // The softmax reads a tile's scores as exponents x = c*s - m, formed in
+    // place by shift() while the previous tile's PV MFMAs run (the vector
+    // ALU is otherwise idle there; this moves one of the four vector
+    // instructions per score out of the exponential phase).  m is finite
+    // from tile 0 on (every query sees key 0), so x never involves an
+    // infinite base.  tsum collects this lane's part of the tile's row sum,
+    // from the fp32 weights (the 16-bit rounding of P, up to 2^-9 relative
+    // for bf16, stays out of l and lse).
+    auto shift = [&](floatx16 (&x)[KB], int kb, int r) __attribute__((always_inline)) {
+        x[kb][r] = fmaf(x[kb][r], c, -m_run);
+    };
     float tsum = 0.f;
     auto softmax_part = [&](const floatx16 (&x)[KB], int kb, int u) __attribute__((always_inline)) {
         if (kb == 0 && u == 0) tsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(x[kb][8 * u + e], c, -m_run));
+            const float p = __builtin_amdgcn_exp2f(x[kb][8 * u + e]);
             tsum += p;
             pb[kb][u][e] = (scalar)p;
         }
     };
-    // Accept the tile's weights, or (rare) raise m to the tile's exact
-    // maximum, rescale O and l, and recompute the weights.  The negated test
-    // also catches an infinite sum.
-    auto accept = [&](const floatx16 (&x)[KB]) __attribute__((always_inline)) {
+    // Accept the tile's weights, or (rare) raise m by the tile's largest
+    // exponent (to the tile's exact row maximum), rescale O and l, shift the
+    // exponents and recompute the weights.  The negated test also catches an
+    // infinite sum.
+    auto accept = [&](floatx16 (&x)[KB]) __attribute__((always_inline)) {
         if (__any(!(tsum <= kTileSumLimit))) {
             // Keep this a real branch: the compiler would otherwise turn it
             // into unconditional work on every tile.
             asm volatile("" ::: "memory");
-            row_max(x);
-            raise_max();
+            float mx = __builtin_elementwise_maximum(x[0][0], x[0][1]);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = kb == 0 ? 2 : 0; r < 16; ++r)
+                    mx = __builtin_elementwise_maximum(mx, x[kb][r]);
+            // delta >= 0; a lane whose keys are all masked has mx = -inf.
+            const float delta = fmaxf(max_halves(mx), 0.f);
+            const float alpha = __builtin_amdgcn_exp2f(-delta);
+            m_run += delta;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[kb][r] -= delta;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -353,6 +378,10 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_ker
     if (n_full == 0) mask(sA, 0);
     row_max(sA);
     raise_max();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) shift(sA, kb, r);
     // Iteration 0 overwrites K0; every wave must be done reading K(0).
     __syncthreads();
 
@@ -387,15 +416,22 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_ker
         __builtin_amdgcn_sched_barrier(0);
         accept(cur);
         __builtin_amdgcn_sched_barrier(0);
-        // Phase 2: PV(j) | mask of tile j+1.
+        // Phase 2: PV(j) | mask and exponents of tile j+1, SPM scores next
+        // to each of the 2*KB*DB MFMAs.
         if constexpr (MASK_NEXT) mask(nxt, j + 1);
+        constexpr int SPM = 16 * KB / (2 * KB * DB);
+        static_assert(SPM * 2 * KB * DB == 16 * KB, "phase 2 must cover every score once");
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
+                for (int db = 0; db < DB; ++db) {
                     oacc[db] = T::mfma32(read_v(vb_cur, kb, u, db), pb[kb][u], oacc[db]);
+                    const int i = SPM * ((kb * 2 + u) * DB + db);
+#pragma unroll
+                    for (int e = 0; e < SPM; ++e) shift(nxt, (i + e) / 16, (i + e) % 16);
+                }
         __builtin_amdgcn_sched_barrier(0);
         wait_vmem();
         __syncthreads();

@@ -97,6 +97,33 @@ def test_lengths(orc, N, causal):
     run_full(orc, 1, 2, N, 128, "bf16", causal, seed=N)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale_mul", [1.0, 8.0])
+def test_running_max_raised_mid_row(orc, dtype, causal, scale_mul):
+    """Keys whose norm grows 8x along the sequence: later key tiles beat the
+    first tile's maximum by far more than 10 (log2 units), so the kernel must
+    raise its running max mid-row (rescaling O and l) on many tiles."""
+    B, H, N, d = 1, 2, 1024, 128
+    print(f"case fwd ramped keys {dtype} causal={causal} scale x{scale_mul}", flush=True)
+    q, k, v = synth.fwd_inputs(B, H, N, d, dtype, seed=77, device=DEV)
+    ramp = torch.linspace(1.0, 8.0, N, device=DEV)[None, None, :, None]
+    k = (k.float() * ramp).to(k.dtype)
+    scale = scale_mul / math.sqrt(d)
+    # The input property the test relies on, checked in fp64 on the CPU.
+    qc, kc = q.double().cpu(), k.double().cpu()
+    s = scale * math.log2(math.e) * (qc @ kc.transpose(-1, -2).contiguous())
+    if causal:
+        s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    gap = (s[..., 64:].amax(-1) - s[..., :64].amax(-1))[..., 64:]
+    assert (gap > 10).float().mean() > 0.5, gap.median()
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = orc.attention(synth.to_bits(q), synth.to_bits(k), synth.to_bits(v), dtype, causal,
+                           scale)
+    assert_close(o.cpu().numpy(), ro, lse.cpu().numpy(), rl, f"ramped keys {dtype} causal={causal}")
+
+
 def test_single_key_returns_v(orc):
     q, k, v = synth.fwd_inputs(2, 4, 1, 128, "bf16", seed=3, device=DEV)
     o, lse = fa.fwd(q, k, v, scale=0.1)
