@@ -46,14 +46,18 @@
 namespace fa {
 
 // Workgroup shape.  Every wave owns 32 queries and every SIMD runs two
-// waves.  Without a mask the workgroup is 8 waves (256 queries, one per CU),
-// so each K/V tile copied into LDS serves twice the queries; with the causal
-// mask it is 4 waves (128 queries, two per CU), which keeps the diagonal
-// tiles that a workgroup must visit, and the tail of the grid, small.
-// Both were picked by measurement on MI355X.
+// waves.  Without a mask and at d = 128 the workgroup is 8 waves (256
+// queries, one per CU), so each K/V tile copied into LDS serves twice the
+// queries; with the causal mask it is 4 waves (128 queries, two per CU),
+// which keeps the diagonal tiles that a workgroup must visit, and the tail
+// of the grid, small.  At d = 64 (half the MFMA work per tile) 4 waves are
+// faster without a mask too.  All picked by measurement on MI355X.
+template <int D, bool CAUSAL>
+constexpr int fwd_waves() { return (CAUSAL || D == 64) ? 4 : 8; }
+
 template <int D, bool CAUSAL>
 struct FwdTile {
-    static constexpr int WAVES = CAUSAL ? 4 : 8;
+    static constexpr int WAVES = fwd_waves<D, CAUSAL>();
     static constexpr int BM = 32 * WAVES;         // queries per workgroup
     static constexpr int KB = 2;                  // 32-key blocks per tile
     static constexpr int BN = 32 * KB;            // keys per tile
@@ -105,13 +109,14 @@ struct Varlen {
 };
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_kernel(
+__global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CAUSAL>())) void fa_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, float *__restrict__ o,
     float *__restrict__ lse, int Nmax, int nq, float c, uint32_t qand, uint32_t qxor,
     Varlen vl) {
     typedef FwdTile<D, CAUSAL> C;
-    static_assert(C::THREADS == (CAUSAL ? 256 : 512) && C::BLOCKS_PER_CU == (CAUSAL ? 2 : 1),
+    static_assert(C::THREADS == 64 * fwd_waves<D, CAUSAL>() &&
+                      C::BLOCKS_PER_CU == 8 / fwd_waves<D, CAUSAL>(),
                   "launch bounds must match the tile shape");
     typedef typename T::vec8 vec8;
     typedef typename T::scalar scalar;
