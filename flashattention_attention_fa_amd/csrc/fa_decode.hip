@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar block-table reads
     const int lj = lane & 15;   // column (query head) / A-operand row
     const int lg = lane >> 4;   // contraction group 0..3
 
