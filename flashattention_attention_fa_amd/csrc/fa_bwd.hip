@@ -160,8 +160,8 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(
 
     // Q and dO fragments (B operand): lane (li, lh) holds row my_q, dims
     // 16t + 8lh .. +8; rows past N read as zero.
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dout + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc_uniform(q + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc_uniform(dout + head, head_bytes);
     vec8 qf[KSTEPS], df[KSTEPS];
     float dl = 0.f;
 #pragma unroll
@@ -257,34 +257,46 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(
     auto tile_step = [&](int j, const uint16_t *kbuf, const uint16_t *vbuf, auto mask_tag)
                          __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
+        static_assert(NB == 2, "two 32-key blocks per tile");
         vec8 dsb[NB][2];
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
-            // S^T and dP^T blocks: lane (li, lh), register r holds key
-            // 32kb + 8(r/4) + 4lh + r%4 of query my_q.
-            floatx16 s, dp;
+        // S^T and dP^T blocks: lane (li, lh), register r holds key
+        // 32kb + 8(r/4) + 4lh + r%4 of query my_q.
+        floatx16 s[NB], dp[NB];
+        auto products = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
             for (int t = 0; t < KSTEPS; ++t) {
-                s = T::mfma32(read_rows(kbuf, kb, t), qf[t], t == 0 ? zero16 : s);
-                dp = T::mfma32(read_rows(vbuf, kb, t), df[t], t == 0 ? zero16 : dp);
+                s[kb] = T::mfma32(read_rows(kbuf, kb, t), qf[t], t == 0 ? zero16 : s[kb]);
+                dp[kb] = T::mfma32(read_rows(vbuf, kb, t), df[t], t == 0 ? zero16 : dp[kb]);
             }
+        };
+        auto weights = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+                float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -lse2));
                 if constexpr (MASK) {
                     const int key = j * BN + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
                     if (key > lim) p = 0.f;
                 }
-                dsb[kb][r >> 3][r & 7] = (scalar)(p * (dp[r] - dl));
+                dsb[kb][r >> 3][r & 7] = (scalar)(p * (dp[kb][r] - dl));
             }
-        }
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
+        };
+        auto dq_part = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
                     acc[db] = T::mfma32(read_tr(kbuf, kb, u, db), dsb[kb][u], acc[db]);
+        };
+        // Each block's vector work runs next to the other block's MFMAs.
+        products(0);
+        __builtin_amdgcn_sched_barrier(0);
+        products(1);
+        weights(0);
+        __builtin_amdgcn_sched_barrier(0);
+        dq_part(0);
+        weights(1);
+        __builtin_amdgcn_sched_barrier(0);
+        dq_part(1);
     };
 
     // Tile j sits in buffer j % 2; tile j+1 is copied while j is computed.
@@ -408,7 +420,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(
 
     // The role's operand (B): K rows for P waves, V rows for dS waves; lane
     // (li, lh) holds key my_k, dims 16t + 8lh .. +8 (zero past N).
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc((role ? v : k) + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc_uniform((role ? v : k) + head, head_bytes);
     vec8 kv[KSTEPS];
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t)

@@ -58,6 +58,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              0x00020000);
 }
 
+// The same for a workgroup-uniform base and size that the compiler may hold
+// in vector registers (e.g. after an integer division, which runs on the
+// vector unit): reading them from the first lane keeps the resource in
+// scalar registers instead of a loop over distinct lane values.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void *base,
+                                                                   uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return make_rsrc((const void *)(uintptr_t)(((uint64_t)hi << 32) | lo),
+                     __builtin_amdgcn_readfirstlane(bytes));
+}
+
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
 }

@@ -7,8 +7,8 @@
 // the smzdm digest (section 6) tells multi-GPU users to check first.
 //
 // Work split: each wave owns 32 queries of one (batch, head); a workgroup
-// is 8 waves (256 queries) without a mask and 4 waves (128 queries) with the
-// causal mask.  Every SIMD runs two waves (at most 256 registers each):
+// is 8 waves (256 queries) without a mask at d = 128 and 4 waves (128
+// queries) otherwise.  Every SIMD runs two waves (at most 256 registers each):
 // while one wave computes exponentials the other keeps the matrix core
 // busy.  Keys stream through
 // LDS in tiles of 64: the K and V tiles of the coming iterations are copied
