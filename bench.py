@@ -190,6 +190,121 @@ def time_bwd(fa, synth, stream, steps, warmup):
             "source_digest": digest}
 
 
+def all_configs(oracle_seconds=3.0):
+    """Every workload of synth.CONFIGS (the tiny case, the forward benchmark
+    shape, the key-scaled causal shape, the 128k causal prefill and the
+    split-KV decode): GPU time from HIP events on the launch stream, the
+    oracle timed on the host on the whole problem (tiny, decode) or on a
+    bounded sample of rows (the three large forwards, extrapolated to the
+    whole problem by its flop rate), and the error of the GPU result on the
+    oracle's rows.  One JSON line per workload."""
+    import numpy as np
+    import torch
+    import flashattention_attention_fa_amd as fa
+    from flashattention_attention_fa_amd import synth
+    from oracle import oracle as oracle_mod
+
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    threads = int(os.environ["OMP_NUM_THREADS"])
+    orc = oracle_mod.get()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def gpu_ms(fn, warmup, steps):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def err(o, ro, lse, rl):
+        o, ro = np.asarray(o, np.float64), np.asarray(ro, np.float64)
+        return {"max_abs": float(np.abs(o - ro).max()),
+                "rel_l2": float(np.linalg.norm(o - ro) / np.linalg.norm(ro)),
+                "lse_max_abs": float(np.abs(np.asarray(lse, np.float64) - rl).max())}
+
+    for name, c in synth.CONFIGS.items():
+        print(f"config {name}", file=sys.stderr, flush=True)
+        if c["kind"] == "decode":
+            B, Hq, Hkv, L, d = c["B"], c["Hq"], c["Hkv"], c["L"], c["d"]
+            ins = [synth.decode_inputs(B, Hq, Hkv, L, d, c["dtype"], seed=c["seed"] + i, device=dev)
+                   for i in range(KV_COPIES)]
+            o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+            ws = torch.empty(fa.decode_workspace_bytes(B, Hq, d, c["nsplit"]), dtype=torch.uint8,
+                             device=dev)
+            call = lambda i: fa.decode(*ins[i % KV_COPIES], nsplit=c["nsplit"], out=o, lse=lse,
+                                       workspace=ws, stream=stream)
+            ms = gpu_ms(call, 5, 40)
+            call(0)
+            torch.cuda.synchronize()
+            q, kc, vc = ins[0]
+            t0 = time.perf_counter()
+            ro, rl = orc.decode(synth.to_bits(q), synth.to_bits(kc), synth.to_bits(vc), c["dtype"])
+            odt = time.perf_counter() - t0
+            flops = 4.0 * B * Hq * L * d
+            nbytes = decode_bytes(B, Hq, Hkv, L, d)
+            rec = {"config": name, "shape": f"decode B{B} Hq{Hq} Hkv{Hkv} L{L} d{d} {c['dtype']} "
+                                              f"nsplit{c['nsplit']}",
+                   "gpu_us": round(ms * 1e3, 2), "value": round(nbytes / ms / 1e6, 1), "unit": "GB/s",
+                   "roofline_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+                   "oracle": {"what": "whole problem", "seconds": round(odt, 2),
+                              "gflops_fp64": round(flops / odt / 1e9, 2), "cores": threads},
+                   "speedup_vs_oracle": round(odt / (ms / 1e3)),
+                   "parity": err(o.cpu().numpy(), ro, lse.cpu().numpy(), rl)}
+            del ins
+        else:
+            B, H, N, d, causal = c["B"], c["H"], c["N"], c["d"], c["causal"]
+            q, k, v = synth.fwd_inputs(B, H, N, d, c["dtype"], seed=c["seed"], device=dev,
+                                       krow_scale=c.get("krow_scale"))
+            o = torch.empty(q.shape, dtype=torch.float32, device=dev)
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+            scale = 1 / math.sqrt(d)
+            call = lambda i: fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse,
+                                    stream=stream)
+            flops = fwd_flops(B, H, N, d, causal)
+            steps = max(3, min(50, int(2e3 / max(flops / 1e12, 1e-3))))
+            ms = gpu_ms(call, 3, steps)
+            qb, kb, vb = synth.to_bits(q), synth.to_bits(k), synth.to_bits(v)
+            if B * H * N <= 4096:
+                rows = synth.sample_rows(B, H, N, B * H * N, seed=1)
+                what = "whole problem"
+            else:
+                # rows visible keys: N (non-causal) or i + 1; size the sample to the time budget
+                per_row = 4.0 * d * (N if not causal else N / 2)
+                n = int(max(64, min(20000, oracle_seconds * 5e9 / per_row)))
+                rows = synth.sample_rows(B, H, N, n, seed=c["seed"])
+                what = f"{len(rows)} random rows (whole problem extrapolated by flop rate)"
+            row_flops = float(np.sum(4.0 * d * (rows[:, 2] + 1 if causal else np.full(len(rows), N))))
+            t0 = time.perf_counter()
+            ro, rl = orc.attention_rows(qb, kb, vb, c["dtype"], rows, causal, scale)
+            odt = time.perf_counter() - t0
+            r = torch.as_tensor(rows, device=dev)
+            og = o[r[:, 0], r[:, 1], r[:, 2]].cpu().numpy()
+            lg = lse[r[:, 0], r[:, 1], r[:, 2]].cpu().numpy()
+            rate = row_flops / odt
+            full_s = flops / rate
+            rec = {"config": name, "shape": f"fwd B{B} H{H} N{N} d{d} {c['dtype']} "
+                                              f"{'causal' if causal else 'non-causal'}"
+                                              + (" K rows x U[0.5,4]" if c.get("krow_scale") else ""),
+                   "gpu_ms": round(ms, 4), "value": round(flops / ms / 1e9, 1), "unit": "TFLOP/s",
+                   "roofline_frac": round(flops / ms / 1e9 / PEAK_MFMA_TFLOPS, 4),
+                   "oracle": {"what": what, "rows": int(len(rows)), "seconds": round(odt, 2),
+                              "gflops_fp64": round(rate / 1e9, 2), "cores": threads,
+                              "whole_problem_seconds": round(full_s, 1)},
+                   "speedup_vs_oracle": round(full_s / (ms / 1e3)),
+                   "parity": err(og, ro, lg, rl)}
+            del q, k, v, o, lse
+        torch.cuda.empty_cache()
+        print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,11 +320,18 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 3 times (the reference "
                          "kernel that scales the HBM byte counters)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="instead of the step: every workload (tiny, forward benchmark shape, "
+                         "key-scaled causal, 128k causal, decode) with its oracle time and "
+                         "parity on the oracle's rows, one JSON line each")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    if args.all_configs:
+        all_configs()
+        return
 
     import torch
     import flashattention_attention_fa_amd as fa
