@@ -27,16 +27,19 @@
 //    32*(t/16) + 16*((t%16)/8) + 8h + t%8 of the tile.  The A operand V^T
 //    gets exactly those keys from four 8-byte transposing LDS reads
 //    (ds_read_b64_tr_b8: each yields 8 consecutive keys of one dim).
-//  * The weights are scaled by 2^6 before rounding, p' = 2^(c*s - m + 6), so
-//    that typical weights sit in E4M3's normal range instead of its
-//    subnormals.  l sums the fp32 p' (the scale cancels in O = sum p'v / l;
-//    lse subtracts it).  E4M3's largest value is 448 = 2^8.8, so every p'
-//    must stay at or below it: the running max m is taken exactly from the
-//    first tile.  Each lane tracks the largest score of its tile next to the
-//    exponentials; if one exceeds m + 2.8 (log2 units, i.e. p' could pass
-//    448), m is raised to the tile's row maximum (O and l rescaled) and the
-//    tile recomputed.  (A cheaper-looking test on the lane sums of p' fires
-//    on almost every tile: 32 weights of up to 64 often sum past 448.)
+//  * The weights are scaled by 2^4 before rounding, p' = 2^(c*s - m + 4), so
+//    that weights down to 2^-10 of the row maximum sit in E4M3's normal
+//    range instead of its subnormals.  l sums the fp32 p' (the scale cancels
+//    in O = sum p'v / l; lse subtracts it).  E4M3's largest value is
+//    448 = 2^8.8, so every p' must stay at or below it: the running max m is
+//    taken exactly from the first tile.  A weight is at most its lane's sum
+//    of the tile, so a tile whose lane sums all stay within 448 is accepted
+//    as is (with weights of at most 16 at the row maximum, the rule); only
+//    otherwise is the tile's row maximum formed, and if a score passes
+//    m + 4.8 (log2 units, i.e. p' could pass 448), m is raised to it (O and
+//    l rescaled) and the tile recomputed.  (With a 2^6 scale the lane sums
+//    pass 448 on almost every tile, and tracking each lane's largest score
+//    instead costs a vector instruction per two scores.)
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -69,8 +72,12 @@ __device__ __forceinline__ int cvt_fp8x4(float a, float b, float c2, float d) {
 
 // The weight scale 2^kPShift.  m is raised when a score passes m + kRaise
 // (log2 units): 2^(kRaise + kPShift) stays below 448, E4M3's largest value.
-constexpr float kPShift = 6.0f;
-constexpr float kRaise = 2.8f;
+// Every weight is at most its lane's tile sum, so a lane sum up to 448 rules
+// out any overflow without looking at the scores; with weights of at most
+// 2^4 at the row maximum such sums are the rule.
+constexpr float kPShift = 4.0f;
+constexpr float kRaise = 4.8f;
+constexpr float kE4M3Max = 448.0f;
 
 template <int D, bool CAUSAL>
 struct Fp8Tile {
@@ -262,9 +269,9 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_fp8
     // P^T operand bytes: dword w = 4kb + (r/4) of pb holds registers
     // 4(w%4) .. +3 of block kb.
     i32x8 pb;
-    float tsum = 0.f, xmax = 0.f;
+    float tsum = 0.f;
     auto softmax_part = [&](const floatx16 (&x)[KB], int kb, int half) __attribute__((always_inline)) {
-        if (kb == 0 && half == 0) { tsum = 0.f; xmax = x[0][0]; }
+        if (kb == 0 && half == 0) tsum = 0.f;
         const float bias = kPShift - m_run;
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
@@ -274,20 +281,25 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_fp8
             for (int e = 0; e < 4; ++e) {
                 p[e] = __builtin_amdgcn_exp2f(fmaf(x[kb][r0 + e], c, bias));
                 tsum += p[e];
-                xmax = __builtin_elementwise_maximum(xmax, x[kb][r0 + e]);
             }
             pb[4 * kb + r0 / 4] = cvt_fp8x4(p[0], p[1], p[2], p[3]);
         }
     };
+    // Accept the tile's weights when every lane sum is within E4M3's range
+    // (the negated test also catches an infinite sum); otherwise look at the
+    // tile's row maximum and, if a score passes m + kRaise, raise m to it,
+    // rescale O and l, and recompute the weights.
     auto accept = [&](const floatx16 (&x)[KB]) __attribute__((always_inline)) {
-        if (__any(!(xmax * c <= m_run + kRaise))) {
+        if (__any(!(tsum <= kE4M3Max))) {
             asm volatile("" ::: "memory");
             row_max(x);
-            raise_max();
+            if (__any(!(mt <= m_run + kRaise))) {
+                raise_max();
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) softmax_part(x, kb, h);
+                    for (int h = 0; h < 2; ++h) softmax_part(x, kb, h);
+            }
         }
         l_run += tsum;
     };
