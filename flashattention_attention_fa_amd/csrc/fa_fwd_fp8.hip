@@ -64,9 +64,14 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t *p) {
 }
 
 // Four fp32 values rounded (to nearest even) to E4M3, packed into the bytes
-// of one dword in order.
+// of one dword in order.  The first conversion writes the low half of a
+// register whose high half the second one overwrites, so its previous
+// content is irrelevant: it comes from an empty asm statement (a constant
+// would cost one register move per dword).
 __device__ __forceinline__ int cvt_fp8x4(float a, float b, float c2, float d) {
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    int any;
+    asm volatile("" : "=v"(any));
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, any, false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c2, d, lo, true);
 }
 
