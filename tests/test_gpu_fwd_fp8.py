@@ -130,3 +130,36 @@ def test_lse_optional_and_deterministic():
     torch.cuda.synchronize()
     assert l2 is None
     assert torch.equal(o1, o2) and torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_max_raised_mid_row(orc, causal, scale_mul=1.0):
+    """Keys whose norm grows 4x along the sequence: later key tiles beat the
+    first tile's maximum by more than 4.8 (log2 units), where a weight scaled
+    by 2^4 could pass E4M3's 448, so the kernel must raise its running max
+    mid-row (rescaling O and l) on many tiles.  (At 4x the scale, lse near
+    45-54, the lse error reaches 1.9e-3, about 4e-5 relative, with this and
+    with the earlier max-tracking kernel alike: the FP8 scores are not the
+    exactly rounded fp32 sums the 1e-3 lse bar assumes at that magnitude.)"""
+    B, H, N, d = 1, 2, 1024, 128
+    print(f"case fwd_fp8 ramped keys causal={causal} scale x{scale_mul}", flush=True)
+    q, _, v, ds = synth.fp8_inputs(B, H, N, d, seed=78, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(78 * 16 + 5)
+    ramp = torch.linspace(1.0, 4.0, N, device=DEV)[None, None, :, None]
+    k = ((torch.randn((B, H, N, d), generator=g, device=DEV) * ramp) / ds)
+    k = k.to(torch.float8_e4m3fn).view(torch.uint8)
+    scale = scale_mul / math.sqrt(d)
+    # The input property the test relies on, checked in fp64 on the CPU.
+    qd = q.view(torch.float8_e4m3fn).double().cpu() * ds
+    kd = k.view(torch.float8_e4m3fn).double().cpu() * ds
+    s = scale * math.log2(math.e) * (qd @ kd.transpose(-1, -2).contiguous())
+    if causal:
+        s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    gap = (s[..., 64:].amax(-1) - s[..., :64].amax(-1))[..., 64:]
+    assert (gap > 4.8).float().mean() > 0.5, gap.median()
+    o, lse = fa.fwd_fp8(q, k, v, q_descale=ds, k_descale=ds, v_descale=ds, causal=causal,
+                        scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = orc.attention_fp8(synth.fp8_bits(q), synth.fp8_bits(k), synth.fp8_bits(v), causal,
+                               scale, ds, ds, ds)
+    check(o.cpu().numpy(), ro, lse.cpu().numpy(), rl, f"fwd_fp8 ramped keys causal={causal}")
