@@ -61,9 +61,15 @@ struct DecTile {
     static constexpr int V_ELEMS = BK * LD;        // per wave
 };
 
-template <int D>
+template <int D, bool PAGED>
 struct DecBuf {
     u32x4 kf[2][D / 32];               // K A-operands, 2 S^T blocks x D/32 steps
+    u32x4 vr[DecTile<D>::VLOADS];      // V rows, staged to LDS
+};
+// Paged: K rows are loaded whole, like V, and staged through LDS as well.
+template <int D>
+struct DecBuf<D, true> {
+    u32x4 kr[DecTile<D>::VLOADS];      // K rows, staged to LDS
     u32x4 vr[DecTile<D>::VLOADS];      // V rows, staged to LDS
 };
 
@@ -89,6 +95,8 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
 
     // V tile staging, one slab per wave; reused for the final merge.
     __shared__ __attribute__((aligned(16))) uint16_t Vs[C::WAVES][C::V_ELEMS];
+    // Paged: the K rows of the step, same layout as the V slab.
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[PAGED ? C::WAVES : 1][PAGED ? C::V_ELEMS : 1];
     __shared__ float sm_m[C::WAVES][C::COLS], sm_l[C::WAVES][C::COLS];
 
     const int tid = threadIdx.x;
@@ -148,21 +156,19 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
 
     // Keys past L read as zero (buffer range check); keys past the shard end
     // are masked out of the softmax below.
-    auto load = [&](DecBuf<D> &bf, int n) {
+    auto load = [&](DecBuf<D, PAGED> &bf, int n) {
         const int key0 = k_lo + C::BK * n;
         if constexpr (PAGED) {
+            // Whole 2*D-byte rows per 16 lanes for both K and V: a head's rows
+            // are Hkv*D elements apart in the pool, and loading each row in
+            // one go keeps its bytes together in the memory requests.
             const size_t hb[2] = {half_base(key0, 0), half_base(key0, 1)};
-#pragma unroll
-            for (int beta = 0; beta < 2; ++beta)
-#pragma unroll
-                for (int t = 0; t < D / 32; ++t)
-                    bf.kf[beta][t] = __builtin_nontemporal_load(
-                        (const u32x4 *)(k + hb[beta] + lj * prow + 32 * t + 8 * lg));
 #pragma unroll
             for (int r = 0; r < C::VLOADS; ++r) {
                 const int row = vrow + C::VROWS * r;   // row / 16 is static per r
-                bf.vr[r] = __builtin_nontemporal_load(
-                    (const u32x4 *)(v + hb[row >> 4] + (row & 15) * prow + 8 * dc));
+                const size_t off = hb[row >> 4] + (row & 15) * prow + 8 * dc;
+                bf.kr[r] = __builtin_nontemporal_load((const u32x4 *)(k + off));
+                bf.vr[r] = __builtin_nontemporal_load((const u32x4 *)(v + off));
             }
         } else {
 #pragma unroll
@@ -182,15 +188,37 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
     for (int db = 0; db < D / 16; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
     uint16_t *vt = Vs[wave];
+    uint16_t *kt = Ks[PAGED ? wave : 0];
     // ds_read_b64_tr_b16 addressing: lane j of group lg points at row
     // 4*lg + j/4, column 4*(j%4) (plus the 16-dim block offset).
     const uint16_t *va = vt + (4 * lg + (lj >> 2)) * LD + 4 * (lj & 3);
 
-    auto compute = [&](const DecBuf<D> &bf, int n) {
+    auto compute = [&](const DecBuf<D, PAGED> &bf, int n) {
         const int key0 = k_lo + C::BK * n;
 #pragma unroll
         for (int r = 0; r < C::VLOADS; ++r)
             *(u32x4 *)(vt + (vrow + C::VROWS * r) * LD + 8 * dc) = bf.vr[r];
+        // K A-operands: lane (lj, lg) holds key 16beta + lj, dims 32t + 8lg..+8.
+        u32x4 kf[2][D / 32];
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int r = 0; r < C::VLOADS; ++r)
+                *(u32x4 *)(kt + (vrow + C::VROWS * r) * LD + 8 * dc) = bf.kr[r];
+            // The K slab is private to this wave (see the V slab below).
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+                for (int t = 0; t < D / 32; ++t)
+                    kf[beta][t] = *(const u32x4 *)(kt + (16 * beta + lj) * LD + 32 * t + 8 * lg);
+        } else {
+#pragma unroll
+            for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+                for (int t = 0; t < D / 32; ++t) kf[beta][t] = bf.kf[beta][t];
+        }
         // S^T block beta: lane (lj, lg), register r holds key key0 + 16beta + 4lg + r.
         floatx4 sc[2];
 #pragma unroll
@@ -198,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
             sc[beta] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < D / 32; ++t)
-                sc[beta] = T::mfma16(as_vec8<vec8>(bf.kf[beta][t]), qf[t], sc[beta]);
+                sc[beta] = T::mfma16(as_vec8<vec8>(kf[beta][t]), qf[t], sc[beta]);
         }
         if (key0 + C::BK > k_hi) {
 #pragma unroll
@@ -245,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
     };
 
     {
-        DecBuf<D> A, B;
+        DecBuf<D, PAGED> A, B;
         int n = wave;
         if (n < nblk) load(A, n);
         for (; n < nblk; n += 2 * C::WAVES) {
