@@ -22,7 +22,8 @@
 //
 // MFMA 16x16x32 (16 columns = up to 16 query heads of one group):
 //   S^T (16 keys x 16 heads) = K (16 x 32 dims) Q^T, K straight from global
-//   memory into A-operand registers; two S^T blocks (32 keys) form the P^T
+//   memory into A-operand registers (paged caches: K rows staged through LDS
+//   like V, see load()); two S^T blocks (32 keys) form the P^T
 //   operand of O^T (16 dims x 16 heads) += V^T (16 dims x 32 keys) P^T, with
 //   V^T read from a row-major LDS copy of the V rows by transposing reads.
 #include "fa_device.hpp"
