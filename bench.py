@@ -190,14 +190,16 @@ def time_bwd(fa, synth, stream, steps, warmup):
             "source_digest": digest}
 
 
-def all_configs(oracle_seconds=3.0):
-    """Every workload of synth.CONFIGS (the tiny case, the forward benchmark
-    shape, the key-scaled causal shape, the 128k causal prefill and the
-    split-KV decode): GPU time from HIP events on the launch stream, the
-    oracle timed on the host on the whole problem (tiny, decode) or on a
-    bounded sample of rows (the three large forwards, extrapolated to the
-    whole problem by its flop rate), and the error of the GPU result on the
-    oracle's rows.  One JSON line per workload."""
+def cpu_baseline_all_configs(oracle_seconds=3.0):
+    """The CPU-baseline leg for every workload of synth.CONFIGS (the tiny
+    case, the forward benchmark shape, the key-scaled causal shape, the 128k
+    causal prefill and the split-KV decode): GPU time from HIP events on the
+    launch stream beside the oracle timed on the host, on the whole problem
+    (tiny, decode) or on a bounded sample of rows (the three large forwards,
+    extrapolated to the whole problem by its flop rate), and the error of
+    the GPU result on the oracle's rows.  One JSON line per workload.  As in
+    cpu_baseline(), the oracle only serves as the baseline and the checker
+    here; the GPU results come from the library alone."""
     import numpy as np
     import torch
     import flashattention_attention_fa_amd as fa
@@ -330,7 +332,7 @@ def main():
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     if args.all_configs:
-        all_configs()
+        cpu_baseline_all_configs()
         return
 
     import torch
