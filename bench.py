@@ -19,7 +19,12 @@ After the timed steps, the FP8 forward (fa_fwd_fp8) is timed on the same
 forward shape with E4M3 inputs and reported in its own "fp8_fwd" object
 against the dense fp8 MFMA peak, and the attention backward (fa_bwd: the dQ
 kernel, then the dK/dV kernel) on the same shape in its own "bwd" object
-(algorithmic FLOPs 2.5x the forward's: five N x N x d products).  Neither is
+(algorithmic FLOPs 2.5x the forward's: five N x N x d products).  Two more
+objects time the variable-length paths: "varlen_fwd" (fa_fwd_varlen on a
+packed batch of eight sequences of mixed lengths, 65536 tokens in all, the
+forward shape's token count, H=32, d=128, fp16, non-causal) and
+"paged_decode" (fa_decode_paged on the decode shape with the caches in
+16-token pages reached through shuffled block tables).  None of these is
 part of the step or of "value".
 
 Prints ONE JSON line.
@@ -46,6 +51,9 @@ PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA (256 CU x 8192 flop/clk x 
 FWD = dict(B=8, H=32, N=8192, d=128, dtype="fp16", causal=False, seed=1002)
 DEC = dict(B=8, Hq=32, Hkv=8, L=32768, d=128, dtype="bf16", nsplit=16, seed=1005)
 KV_COPIES = 4                 # decode rotates among this many caches (4 GiB > 256 MB MALL)
+VARLEN = dict(lens=(16384, 12288, 9216, 8192, 7168, 6144, 4096, 2048), H=32, d=128,
+              dtype="fp16", causal=False, seed=1007)
+PAGED = dict(DEC, page=16, seed=1008)
 
 
 def fwd_flops(B, H, N, d, causal):
@@ -190,6 +198,99 @@ def time_bwd(fa, synth, stream, steps, warmup):
             "source_digest": digest}
 
 
+def time_varlen(fa, synth, stream, steps, warmup):
+    """fa_fwd_varlen on a packed [T, H, d] batch of mixed lengths: average
+    launch time from HIP events on the launch stream.  FLOPs are the sum of
+    each sequence's own 4*H*L^2*d."""
+    import torch
+    c = VARLEN
+    T = sum(c["lens"])
+    q, k, v = (synth.normal((T, c["H"], c["d"]), c["seed"] * 16 + i, c["dtype"], stream.device)
+               for i in range(3))
+    cu = torch.tensor([0] + [sum(c["lens"][:i + 1]) for i in range(len(c["lens"]))],
+                      dtype=torch.int32, device=stream.device)
+    o = torch.empty((T, c["H"], c["d"]), dtype=torch.float32, device=stream.device)
+    lse = torch.empty((c["H"], T), dtype=torch.float32, device=stream.device)
+    kw = dict(causal=c["causal"], scale=1 / math.sqrt(c["d"]), out=o, lse=lse, stream=stream)
+    for _ in range(warmup):
+        fa.fwd_varlen(q, k, v, cu, max(c["lens"]), **kw)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fa.fwd_varlen(q, k, v, cu, max(c["lens"]), **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = sum(fwd_flops(1, c["H"], L, c["d"], c["causal"]) for L in c["lens"])
+    tf = flops / (ms * 1e-3) / 1e12
+    digest = source_digest("fa_fwd.hip", "fa_device.hpp")
+    return {"kernel": "fa_fwd_kernel (VARLEN)", "bound": "mfma", "dtype": c["dtype"],
+            "workload": f"attention forward, packed batch of {len(c['lens'])} sequences "
+                        f"(lengths {'/'.join(str(L) for L in c['lens'])}, {T} tokens) "
+                        f"H{c['H']} d{c['d']} {c['dtype']} "
+                        f"{'causal' if c['causal'] else 'non-causal'}",
+            "achieved": round(tf, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_MFMA_TFLOPS, 4), "avg_launch_ms": round(ms, 4),
+            "algorithmic_flops_per_launch": flops, "steps": steps,
+            "traffic": load_traffic("fa_fwd_varlen_kernel", digest), "source_digest": digest}
+
+
+def time_paged(fa, synth, stream, steps, warmup):
+    """fa_decode_paged on the decode shape, caches in pages of PAGED["page"]
+    tokens ([num_pages, page, Hkv, d] pools) in shuffled order: average call
+    time from HIP events on the launch stream, rotating among KV_COPIES
+    pools as the dense decode does."""
+    import numpy as np
+    import torch
+    c = PAGED
+    B, P = c["B"], c["page"]
+    pps = c["L"] // P
+    pools = []
+    for i in range(KV_COPIES):
+        rng = np.random.default_rng(c["seed"] + i)
+        table = torch.from_numpy(rng.permutation(B * pps).astype(np.int32).reshape(B, pps))
+        kp, vp = (synth.normal((B * pps, P, c["Hkv"], c["d"]), (c["seed"] + i) * 16 + j,
+                               c["dtype"], stream.device) for j in (1, 2))
+        pools.append((kp, vp, table.to(stream.device)))
+    q = synth.normal((B, c["Hq"], c["d"]), c["seed"] * 16, c["dtype"], stream.device)
+    seq = torch.full((B,), c["L"], dtype=torch.int32, device=stream.device)
+    o = torch.empty((B, c["Hq"], c["d"]), dtype=torch.float32, device=stream.device)
+    lse = torch.empty((B, c["Hq"]), dtype=torch.float32, device=stream.device)
+    ws = torch.empty(fa.decode_workspace_bytes(B, c["Hq"], c["d"], c["nsplit"]), dtype=torch.uint8,
+                     device=stream.device)
+
+    def call(i):
+        kp, vp, table = pools[i % KV_COPIES]
+        fa.decode_paged(q, kp, vp, table, seq, nsplit=c["nsplit"], out=o, lse=lse, workspace=ws,
+                        stream=stream)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = decode_bytes(B, c["Hq"], c["Hkv"], c["L"], c["d"])
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    digest = source_digest("fa_decode.hip", "fa_device.hpp")
+    return {"kernels": "fa_decode_split_kernel (PAGED) + fa_decode_combine_kernel", "bound": "hbm",
+            "dtype": c["dtype"],
+            "workload": f"paged split-KV decode B{B} Hq{c['Hq']} Hkv{c['Hkv']} L{c['L']} "
+                        f"d{c['d']} {c['dtype']} nsplit{c['nsplit']}, {P}-token pages, "
+                        f"shuffled block tables",
+            "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "avg_call_us": round(ms * 1e3, 2),
+            "algorithmic_bytes_per_call": nbytes, "steps": steps,
+            "kv_cache_copies_rotated": KV_COPIES,
+            "traffic": load_traffic("fa_decode_paged_split_kernel", digest),
+            "source_digest": digest}
+
+
 def cpu_baseline_all_configs(oracle_seconds=3.0):
     """The CPU-baseline leg for every workload of synth.CONFIGS (the tiny
     case, the forward benchmark shape, the key-scaled causal shape, the 128k
@@ -317,6 +418,10 @@ def main():
                     help="timed calls of the FP8 forward on the forward shape (0 skips it)")
     ap.add_argument("--bwd-steps", type=int, default=20,
                     help="timed fa_bwd calls for the bwd object (0: skip)")
+    ap.add_argument("--varlen-steps", type=int, default=20,
+                    help="timed fa_fwd_varlen calls for the varlen_fwd object (0: skip)")
+    ap.add_argument("--paged-steps", type=int, default=50,
+                    help="timed fa_decode_paged calls for the paged_decode object (0: skip)")
     ap.add_argument("--only", choices=["fwd", "decode"], default=None,
                     help="time one call only (for profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -463,6 +568,10 @@ def main():
         out["fp8_fwd"] = time_fp8(fa, synth, stream, args.fp8_steps, max(5, args.warmup // 2))
     if args.bwd_steps > 0 and args.only is None:
         out["bwd"] = time_bwd(fa, synth, stream, args.bwd_steps, 3)
+    if args.varlen_steps > 0 and args.only is None:
+        out["varlen_fwd"] = time_varlen(fa, synth, stream, args.varlen_steps, 3)
+    if args.paged_steps > 0 and args.only is None:
+        out["paged_decode"] = time_paged(fa, synth, stream, args.paged_steps, 5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
