@@ -51,9 +51,6 @@ PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA (256 CU x 8192 flop/clk x 
 FWD = dict(B=8, H=32, N=8192, d=128, dtype="fp16", causal=False, seed=1002)
 DEC = dict(B=8, Hq=32, Hkv=8, L=32768, d=128, dtype="bf16", nsplit=16, seed=1005)
 KV_COPIES = 4                 # decode rotates among this many caches (4 GiB > 256 MB MALL)
-VARLEN = dict(lens=(16384, 12288, 9216, 8192, 7168, 6144, 4096, 2048), H=32, d=128,
-              dtype="fp16", causal=False, seed=1007)
-PAGED = dict(DEC, page=16, seed=1008)
 
 
 def fwd_flops(B, H, N, d, causal):
@@ -203,12 +200,10 @@ def time_varlen(fa, synth, stream, steps, warmup):
     launch time from HIP events on the launch stream.  FLOPs are the sum of
     each sequence's own 4*H*L^2*d."""
     import torch
-    c = VARLEN
+    c = synth.VARLEN_BENCH
     T = sum(c["lens"])
-    q, k, v = (synth.normal((T, c["H"], c["d"]), c["seed"] * 16 + i, c["dtype"], stream.device)
-               for i in range(3))
-    cu = torch.tensor([0] + [sum(c["lens"][:i + 1]) for i in range(len(c["lens"]))],
-                      dtype=torch.int32, device=stream.device)
+    q, k, v, cu = synth.varlen_inputs(c["lens"], c["H"], c["d"], c["dtype"], seed=c["seed"],
+                                      device=stream.device)
     o = torch.empty((T, c["H"], c["d"]), dtype=torch.float32, device=stream.device)
     lse = torch.empty((c["H"], T), dtype=torch.float32, device=stream.device)
     kw = dict(causal=c["causal"], scale=1 / math.sqrt(c["d"]), out=o, lse=lse, stream=stream)
@@ -237,31 +232,23 @@ def time_varlen(fa, synth, stream, steps, warmup):
 
 
 def time_paged(fa, synth, stream, steps, warmup):
-    """fa_decode_paged on the decode shape, caches in pages of PAGED["page"]
+    """fa_decode_paged on the decode shape, caches in pages of c["page"]
     tokens ([num_pages, page, Hkv, d] pools) in shuffled order: average call
     time from HIP events on the launch stream, rotating among KV_COPIES
-    pools as the dense decode does."""
-    import numpy as np
+    input sets (seeds seed + i) as the dense decode does."""
     import torch
-    c = PAGED
+    c = synth.PAGED_BENCH
     B, P = c["B"], c["page"]
-    pps = c["L"] // P
-    pools = []
-    for i in range(KV_COPIES):
-        rng = np.random.default_rng(c["seed"] + i)
-        table = torch.from_numpy(rng.permutation(B * pps).astype(np.int32).reshape(B, pps))
-        kp, vp = (synth.normal((B * pps, P, c["Hkv"], c["d"]), (c["seed"] + i) * 16 + j,
-                               c["dtype"], stream.device) for j in (1, 2))
-        pools.append((kp, vp, table.to(stream.device)))
-    q = synth.normal((B, c["Hq"], c["d"]), c["seed"] * 16, c["dtype"], stream.device)
-    seq = torch.full((B,), c["L"], dtype=torch.int32, device=stream.device)
+    pools = [synth.paged_decode_inputs(B, c["Hq"], c["Hkv"], c["L"], c["d"], P, c["dtype"],
+                                       seed=c["seed"] + i, device=stream.device)
+             for i in range(KV_COPIES)]
     o = torch.empty((B, c["Hq"], c["d"]), dtype=torch.float32, device=stream.device)
     lse = torch.empty((B, c["Hq"]), dtype=torch.float32, device=stream.device)
     ws = torch.empty(fa.decode_workspace_bytes(B, c["Hq"], c["d"], c["nsplit"]), dtype=torch.uint8,
                      device=stream.device)
 
     def call(i):
-        kp, vp, table = pools[i % KV_COPIES]
+        q, kp, vp, table, seq = pools[i % KV_COPIES]
         fa.decode_paged(q, kp, vp, table, seq, nsplit=c["nsplit"], out=o, lse=lse, workspace=ws,
                         stream=stream)
 

@@ -87,6 +87,34 @@ def decode_inputs(B, Hq, Hkv, L, d, dtype="bf16", seed=0, device="cpu"):
     return q, k, v
 
 
+def varlen_inputs(lens, H, d, dtype="bf16", seed=0, device="cpu"):
+    """A packed batch of len(lens) sequences: q, k, v [T, H, d] i.i.d. N(0,1)
+    with T = sum(lens) (seeds as fwd_inputs), and cu_seqlens [B+1] int32."""
+    base = int(seed) * 16
+    T = int(sum(lens))
+    q, k, v = (normal((T, H, d), base + i, dtype, device) for i in range(3))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=device)
+    return q, k, v, cu
+
+
+def paged_decode_inputs(B, Hq, Hkv, L, d, page, dtype="bf16", seed=0, device="cpu"):
+    """Decode inputs with the caches in pages: q [B, Hq, d]; K and V pools
+    [B*L/page, page, Hkv, d] i.i.d. N(0,1); a block table [B, L/page] int32
+    holding a seeded permutation of the pools' pages (key j of sequence b is
+    slot j % page of page table[b, j // page]); seq_lens [B] int32, all L."""
+    if L % page:
+        raise ValueError("L must be a multiple of the page size")
+    pps = L // page
+    base = int(seed) * 16
+    rng = np.random.default_rng(int(seed))
+    table = torch.from_numpy(rng.permutation(B * pps).astype(np.int32).reshape(B, pps)).to(device)
+    q = normal((B, Hq, d), base + 0, dtype, device)
+    kp = normal((B * pps, page, Hkv, d), base + 1, dtype, device)
+    vp = normal((B * pps, page, Hkv, d), base + 2, dtype, device)
+    seq = torch.full((B,), L, dtype=torch.int32, device=device)
+    return q, kp, vp, table, seq
+
+
 def to_bits(t: torch.Tensor) -> np.ndarray:
     """16-bit tensor -> host numpy uint16 bit patterns (what the oracle reads)."""
     if t.dtype not in (torch.bfloat16, torch.float16):
@@ -142,3 +170,10 @@ CONFIGS = {
     "decode_b8hq32hkv8l32k": dict(kind="decode", B=8, Hq=32, Hkv=8, L=32768, d=128, dtype="bf16",
                                   nsplit=16, seed=1005),
 }
+
+# The workloads of bench.py's variable-length legs: one packed batch of
+# mixed lengths with the forward shape's 65536 tokens, and the decode shape
+# in 16-token pages.
+VARLEN_BENCH = dict(lens=(16384, 12288, 9216, 8192, 7168, 6144, 4096, 2048), H=32, d=128,
+                    dtype="fp16", causal=False, seed=1007)
+PAGED_BENCH = dict(B=8, Hq=32, Hkv=8, L=32768, d=128, dtype="bf16", nsplit=16, page=16, seed=1008)

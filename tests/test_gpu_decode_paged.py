@@ -104,3 +104,29 @@ def test_matches_dense_layout():
     o_p, l_p = fa.decode_paged(q, kpages, vpages, table, seq, nsplit=8)
     torch.cuda.synchronize()
     assert torch.equal(o_d, o_p) and torch.equal(l_d, l_p)
+
+
+def test_bench_shape(orc):
+    """The workload bench.py's paged_decode leg times (B8 Hq32 Hkv8 L32768
+    d128 bf16, 16-token pages in shuffled order, nsplit 16, the same launch):
+    every query head of every sequence against the oracle on the keys
+    gathered through the block table."""
+    c = synth.PAGED_BENCH
+    B, page = c["B"], c["page"]
+    print(f"case decode_paged bench shape B{B} Hq{c['Hq']} Hkv{c['Hkv']} L{c['L']} page{page}",
+          flush=True)
+    q, kp, vp, table, seq = synth.paged_decode_inputs(B, c["Hq"], c["Hkv"], c["L"], c["d"], page,
+                                                      c["dtype"], seed=c["seed"], device=DEV)
+    o, lse = fa.decode_paged(q, kp, vp, table, seq, nsplit=c["nsplit"])
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    qb, kb, vb = synth.to_bits(q), synth.to_bits(kp), synth.to_bits(vp)
+    del kp, vp
+    table_np = table.cpu().numpy()
+    ro = np.zeros(o.shape, np.float64)
+    rl = np.zeros(lse.shape, np.float64)
+    for b in range(B):
+        kc, vc = gather(kb, table_np[b], c["L"], page), gather(vb, table_np[b], c["L"], page)
+        rob, rlb = orc.decode(qb[b:b + 1], kc, vc, c["dtype"])
+        ro[b], rl[b] = rob[0], rlb[0]
+    assert_close(o, ro, lse, rl, f"decode_paged bench shape nsplit{c['nsplit']}")

@@ -71,3 +71,33 @@ def test_equal_lengths_match_dense():
         torch.cuda.synchronize()
         assert torch.equal(o_p, o_d.permute(0, 2, 1, 3).reshape(B * N, H, d))
         assert torch.equal(l_p, l_d.permute(1, 0, 2).reshape(H, B * N))
+
+
+def test_bench_batch_sampled(orc):
+    """The batch bench.py's varlen_fwd leg times (8 packed sequences, 65536
+    tokens, H32 d128 fp16, the same launch): boundary and random rows of
+    every sequence against the oracle run on that sequence alone."""
+    c = synth.VARLEN_BENCH
+    lens, H, d = c["lens"], c["H"], c["d"]
+    print(f"case fwd_varlen bench batch lens={lens} H{H} d{d} {c['dtype']}", flush=True)
+    q, k, v, cu = synth.varlen_inputs(lens, H, d, c["dtype"], seed=c["seed"], device=DEV)
+    scale = 1 / math.sqrt(d)
+    o, lse = fa.fwd_varlen(q, k, v, cu, max(lens), causal=c["causal"], scale=scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    qb, kb, vb = synth.to_bits(q), synth.to_bits(k), synth.to_bits(v)
+    del q, k, v
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    start = 0
+    for n, L in enumerate(lens):
+        rows = synth.boundary_rows(1, H, L, seed=c["seed"] + n, tiles=(64, 128, 256), n_random=24)
+        sl = slice(start, start + L)
+        per = [np.ascontiguousarray(x[sl].transpose(1, 0, 2)[None]) for x in (qb, kb, vb)]
+        ro, rl = orc.attention_rows(*per, c["dtype"], rows, c["causal"], scale)
+        got_o.append(o[start + rows[:, 2], rows[:, 1]])
+        got_l.append(lse[rows[:, 1], start + rows[:, 2]])
+        ref_o.append(ro)
+        ref_l.append(rl)
+        start += L
+    assert_close(np.concatenate(got_o), np.concatenate(ref_o), np.concatenate(got_l),
+                 np.concatenate(ref_l), f"fwd_varlen bench batch {sum(len(x) for x in got_o)} rows")
