@@ -281,7 +281,8 @@ def time_paged(fa, synth, stream, steps, warmup):
 def cpu_baseline_all_configs(oracle_seconds=3.0):
     """The CPU-baseline leg for every workload of synth.CONFIGS (the tiny
     case, the forward benchmark shape, the key-scaled causal shape, the 128k
-    causal prefill and the split-KV decode): GPU time from HIP events on the
+    causal prefill and the split-KV decode) and of the two variable-length
+    bench legs (synth.VARLEN_BENCH, synth.PAGED_BENCH): GPU time from HIP events on the
     launch stream beside the oracle timed on the host, on the whole problem
     (tiny, decode) or on a bounded sample of rows (the three large forwards,
     extrapolated to the whole problem by its flop rate), and the error of
@@ -394,6 +395,97 @@ def cpu_baseline_all_configs(oracle_seconds=3.0):
         torch.cuda.empty_cache()
         print(json.dumps(rec), flush=True)
 
+    # The variable-length bench legs: the packed batch (sampled rows of every
+    # sequence, oracle run on that sequence alone) and the paged decode
+    # (whole problem, keys gathered through the block table on the host).
+    c = synth.VARLEN_BENCH
+    print("config varlen_bench", file=sys.stderr, flush=True)
+    lens, H, d = c["lens"], c["H"], c["d"]
+    q, k, v, cu = synth.varlen_inputs(lens, H, d, c["dtype"], seed=c["seed"], device=dev)
+    T = sum(lens)
+    o = torch.empty((T, H, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    scale = 1 / math.sqrt(d)
+    call = lambda i: fa.fwd_varlen(q, k, v, cu, max(lens), causal=c["causal"], scale=scale, out=o,
+                                   lse=lse, stream=stream)
+    flops = sum(fwd_flops(1, H, L, d, c["causal"]) for L in lens)
+    ms = gpu_ms(call, 3, 20)
+    call(0)
+    torch.cuda.synchronize()
+    og_all, lg_all = o.cpu().numpy(), lse.cpu().numpy()
+    qb, kb, vb = synth.to_bits(q), synth.to_bits(k), synth.to_bits(v)
+    del q, k, v, o, lse
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    row_flops, odt, start = 0.0, 0.0, 0
+    for n, L in enumerate(lens):
+        nrow = int(max(16, oracle_seconds * 5e9 / len(lens) / (4.0 * d * L)))
+        rows = synth.sample_rows(1, H, L, nrow, seed=c["seed"] + n)
+        sl = slice(start, start + L)
+        per = [np.ascontiguousarray(x[sl].transpose(1, 0, 2)[None]) for x in (qb, kb, vb)]
+        t0 = time.perf_counter()
+        ro, rl = orc.attention_rows(*per, c["dtype"], rows, c["causal"], scale)
+        odt += time.perf_counter() - t0
+        row_flops += 4.0 * d * L * len(rows)
+        got_o.append(og_all[start + rows[:, 2], rows[:, 1]])
+        got_l.append(lg_all[rows[:, 1], start + rows[:, 2]])
+        ref_o.append(ro)
+        ref_l.append(rl)
+        start += L
+    rate = row_flops / odt
+    nrows = sum(len(x) for x in got_o)
+    rec = {"config": "varlen_bench", "shape": f"fwd varlen {len(lens)} packed sequences "
+                                             f"{'/'.join(map(str, lens))} ({T} tokens) H{H} d{d} "
+                                             f"{c['dtype']} {'causal' if c['causal'] else 'non-causal'}",
+           "gpu_ms": round(ms, 4), "value": round(flops / ms / 1e9, 1), "unit": "TFLOP/s",
+           "roofline_frac": round(flops / ms / 1e9 / PEAK_MFMA_TFLOPS, 4),
+           "oracle": {"what": f"{nrows} random rows (whole problem extrapolated by flop rate)",
+                      "rows": nrows, "seconds": round(odt, 2), "gflops_fp64": round(rate / 1e9, 2),
+                      "cores": threads, "whole_problem_seconds": round(flops / rate, 1)},
+           "speedup_vs_oracle": round(flops / rate / (ms / 1e3)),
+           "parity": err(np.concatenate(got_o), np.concatenate(ref_o), np.concatenate(got_l),
+                         np.concatenate(ref_l))}
+    del qb, kb, vb
+    torch.cuda.empty_cache()
+    print(json.dumps(rec), flush=True)
+
+    c = synth.PAGED_BENCH
+    print("config paged_bench", file=sys.stderr, flush=True)
+    B, Hq, Hkv, L, d, P = c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], c["page"]
+    ins = [synth.paged_decode_inputs(B, Hq, Hkv, L, d, P, c["dtype"], seed=c["seed"] + i, device=dev)
+           for i in range(KV_COPIES)]
+    o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_workspace_bytes(B, Hq, d, c["nsplit"]), dtype=torch.uint8, device=dev)
+    call = lambda i: fa.decode_paged(*ins[i % KV_COPIES], nsplit=c["nsplit"], out=o, lse=lse,
+                                     workspace=ws, stream=stream)
+    ms = gpu_ms(call, 5, 40)
+    call(0)
+    torch.cuda.synchronize()
+    q, kp, vp, table, _ = ins[0]
+    qb, kpb, vpb, tb = synth.to_bits(q), synth.to_bits(kp), synth.to_bits(vp), table.cpu().numpy()
+    del ins
+    idx = np.arange(L)
+    odt = 0.0
+    ro, rl = np.zeros((B, Hq, d)), np.zeros((B, Hq))
+    for b in range(B):
+        kc, vc = (np.ascontiguousarray(x[tb[b, idx // P], idx % P].transpose(1, 0, 2)[None])
+                  for x in (kpb, vpb))
+        t0 = time.perf_counter()
+        rob, rlb = orc.decode(qb[b:b + 1], kc, vc, c["dtype"])
+        odt += time.perf_counter() - t0
+        ro[b], rl[b] = rob[0], rlb[0]
+    nbytes = decode_bytes(B, Hq, Hkv, L, d)
+    rec = {"config": "paged_bench", "shape": f"paged decode B{B} Hq{Hq} Hkv{Hkv} L{L} d{d} "
+                                            f"{c['dtype']} nsplit{c['nsplit']} page{P}",
+           "gpu_us": round(ms * 1e3, 2), "value": round(nbytes / ms / 1e6, 1), "unit": "GB/s",
+           "roofline_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+           "oracle": {"what": "whole problem (keys gathered through the block table first, "
+                              "not timed)", "seconds": round(odt, 2),
+                      "gflops_fp64": round(4.0 * B * Hq * L * d / odt / 1e9, 2), "cores": threads},
+           "speedup_vs_oracle": round(odt / (ms / 1e3)),
+           "parity": err(o.cpu().numpy(), ro, lse.cpu().numpy(), rl)}
+    print(json.dumps(rec), flush=True)
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
@@ -416,8 +508,9 @@ def main():
                          "kernel that scales the HBM byte counters)")
     ap.add_argument("--all-configs", action="store_true",
                     help="instead of the step: every workload (tiny, forward benchmark shape, "
-                         "key-scaled causal, 128k causal, decode) with its oracle time and "
-                         "parity on the oracle's rows, one JSON line each")
+                         "key-scaled causal, 128k causal, decode, varlen batch, paged decode) "
+                         "with its oracle time and parity on the oracle's rows, one JSON line "
+                         "each")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
