@@ -265,7 +265,7 @@ def time_paged(fa, synth, stream, steps, warmup):
     nbytes = decode_bytes(B, c["Hq"], c["Hkv"], c["L"], c["d"])
     gbs = nbytes / (ms * 1e-3) / 1e9
     digest = source_digest("fa_decode.hip", "fa_device.hpp")
-    return {"kernels": "fa_decode_split_kernel (PAGED) + fa_decode_combine_kernel", "bound": "hbm",
+    return {"kernels": "fa_decode_split_kernel (PAGED) + fa_decode_combine_few_kernel<16>", "bound": "hbm",
             "dtype": c["dtype"],
             "workload": f"paged split-KV decode B{B} Hq{c['Hq']} Hkv{c['Hkv']} L{c['L']} "
                         f"d{c['d']} {c['dtype']} nsplit{c['nsplit']}, {P}-token pages, "
@@ -629,7 +629,7 @@ def main():
             "source_digest": fwd_digest,
         },
         "decode": {
-            "kernels": "fa_decode_split_kernel + fa_decode_combine_kernel",
+            "kernels": "fa_decode_split_kernel + fa_decode_combine_few_kernel<16>",
             "bound": "hbm",
             "achieved": round(gbs, 1),
             "peak": PEAK_HBM_GBS,

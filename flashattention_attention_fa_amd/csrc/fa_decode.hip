@@ -346,6 +346,39 @@ __device__ __forceinline__ float block_sum128(float x, float *red) {
     return x;
 }
 
+// Combine for at most NS shards: every thread loads all shard lse values and
+// its output dim of every shard at once (one memory round trip) and forms
+// the weights itself (base-2 exponentials of log2(e)-scaled differences).
+template <int NS>
+__global__ __launch_bounds__(128) void fa_decode_combine_few_kernel(
+    const float *__restrict__ ws_o, const float *__restrict__ ws_lse,
+    float *__restrict__ o, float *__restrict__ lse, int D, int nsplit) {
+    const int tid = threadIdx.x;
+    const size_t row = blockIdx.x;
+    const float *pl = ws_lse + row * nsplit;
+    const float *po = ws_o + row * (size_t)nsplit * D;
+    const bool mine = tid < D;
+    float lv[NS], ov[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        lv[s] = s < nsplit ? pl[s] : -INFINITY;
+        ov[s] = (s < nsplit && mine) ? po[(size_t)s * D + tid] : 0.f;
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) M = fmaxf(M, lv[s]);
+    const float mb = M == -INFINITY ? 0.f : M;
+    float wsum = 0.f, acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const float w = __builtin_amdgcn_exp2f((lv[s] - mb) * kLog2e);
+        wsum += w;
+        acc = fmaf(w, ov[s], acc);
+    }
+    if (mine) o[row * D + tid] = M == -INFINITY ? 0.f : acc / wsum;
+    if (lse != nullptr && tid == 0) lse[row] = M == -INFINITY ? -INFINITY : M + logf(wsum);
+}
+
 // Combine: one 128-thread workgroup per (batch, query head).  The shard
 // weights exp(lse_s - lse) are computed once per shard and shared via LDS;
 // each thread then sums one output dim over the shards.
@@ -408,8 +441,15 @@ static hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
                            a.Hq, a.Hkv, a.L, a.nsplit, a.chunk, ncc, c, pc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fa_decode_combine_kernel, dim3(a.B * a.Hq), dim3(128), 0, stream,
-                       a.ws_o, a.ws_lse, a.o, a.lse, D, a.nsplit);
+    if (a.nsplit <= 16)
+        hipLaunchKernelGGL(fa_decode_combine_few_kernel<16>, dim3(a.B * a.Hq), dim3(128), 0, stream,
+                           a.ws_o, a.ws_lse, a.o, a.lse, D, a.nsplit);
+    else if (a.nsplit <= 32)
+        hipLaunchKernelGGL(fa_decode_combine_few_kernel<32>, dim3(a.B * a.Hq), dim3(128), 0, stream,
+                           a.ws_o, a.ws_lse, a.o, a.lse, D, a.nsplit);
+    else
+        hipLaunchKernelGGL(fa_decode_combine_kernel, dim3(a.B * a.Hq), dim3(128), 0, stream,
+                           a.ws_o, a.ws_lse, a.o, a.lse, D, a.nsplit);
     return hipGetLastError();
 }
 
