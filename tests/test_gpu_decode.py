@@ -40,9 +40,12 @@ def test_long_cache(orc):
 
 
 @pytest.mark.parametrize("L,nsplit", [(1, 1), (1, 4), (5, 4), (31, 1), (33, 2), (1000, 7),
-                                      (777, 16), (64, 64), (40, 100), (4096, 3), (2049, 16)])
+                                      (777, 16), (64, 64), (40, 100), (4096, 3), (2049, 16),
+                                      (1000, 24), (5000, 32), (20, 17), (3000, 33)])
 def test_split_counts(orc, L, nsplit):
-    run(orc, 2, 8, 2, L, 128, nsplit, seed=L)
+    """Shard counts on both sides of the combine's forms: up to 16, 17-32
+    (one-round-trip kernels) and above 32 (LDS form), with empty shards."""
+    run(orc, 2, 8, 2, L, 128, nsplit, seed=L + nsplit)
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 1), (16, 2), (20, 1), (32, 1), (48, 2)])

@@ -79,7 +79,7 @@ def test_page_sizes(orc, page):
     run(orc, [1, 17, 100, 777, 2048, 0, 3000], 8, 2, 128, page, nsplit=5, seed=page)
 
 
-@pytest.mark.parametrize("nsplit", [1, 3, 16, 64])
+@pytest.mark.parametrize("nsplit", [1, 3, 16, 24, 64])
 def test_split_counts(orc, nsplit):
     run(orc, [5, 64, 1000, 4096], 8, 2, 128, 32, nsplit=nsplit, seed=100 + nsplit)
 
