@@ -177,3 +177,27 @@ def test_empty_batch_is_noop():
     q = torch.empty(0, 2, 16, 64, dtype=torch.bfloat16, device=DEV)
     o, lse = fa.fwd(q, q, q)
     assert o.numel() == 0 and lse.numel() == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_score_dot_products_keep_fp32_range(dtype):
+    """One key per head (N = 1, scale 1: lse = q.k).  A product 2^16 next to
+    127 products of 2^-6 in the same group of dims: the exact sum
+    65536 + 127/64 is representable in fp32, and the 16-bit matrix cores keep
+    it (products 22 binades below the largest survive), unlike the FP8 form,
+    which drops products 14 binades down; the 1e-3 lse bar of the 16-bit
+    path rests on this."""
+    H = 8
+    q = torch.ones(1, H, 1, 128)
+    k = torch.full((1, H, 1, 128), 2.0 ** -6)
+    for h in range(H):
+        q[0, h, 0, 8 * h % 128] = 256.0
+        k[0, h, 0, 8 * h % 128] = 256.0
+    t = torch.bfloat16 if dtype == "bf16" else torch.float16
+    assert torch.equal(q.to(t).float(), q) and torch.equal(k.to(t).float(), k)
+    print(f"case fwd score range {dtype}", flush=True)
+    _, lse = fa.fwd(q.to(t).to(DEV), k.to(t).to(DEV), q.to(t).to(DEV), scale=1.0)
+    torch.cuda.synchronize()
+    exact = 65536.0 + 127 / 64
+    # fp32 rounding of c*s and of the final product: a few ulp of 9.5e4
+    np.testing.assert_allclose(lse.cpu().double().numpy(), exact, rtol=0, atol=0.05)
