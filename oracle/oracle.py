@@ -86,6 +86,11 @@ class Oracle:
     def widen(self, bits: int, dtype: str) -> float:
         return self.lib.oracle_widen(int(bits), DTYPES[dtype])
 
+    def widen_many(self, bits, dtype: str) -> np.ndarray:
+        """oracle_widen of every pattern in ``bits``, one call each."""
+        f, t = self.lib.oracle_widen, DTYPES[dtype]
+        return np.array([f(int(b), t) for b in np.asarray(bits).ravel()], dtype=np.float64)
+
     # -- attention over explicit rows ---------------------------------------
     def attention_rows(self, q, k, v, dtype: str, rows, causal: bool,
                        scale: float, klo: int = 0, khi: int | None = None):

@@ -4,7 +4,8 @@ The forward that feeds the backward (O, lse) is this library's fa_fwd on the
 same inputs, as a training step would run it.  Bar per gradient tensor:
 rel-L2 <= 5e-3 and max |g - g_ref| <= 2e-2 * max |g_ref| (the weights P and
 dS are rounded to the 16-bit storage type for their products, a relative
-error of at most 2^-9 for bf16 per element, accumulated in fp32).
+error of at most 2^-8 for bf16 and 2^-11 for fp16 per element (round to
+nearest with 8 and 11 significant bits), accumulated in fp32).
 """
 import math
 

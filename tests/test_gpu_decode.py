@@ -117,7 +117,9 @@ def test_workspace_reuse_across_calls():
 def test_split_equals_unsplit_closely():
     """Different shard counts give the same attention up to rounding: the
     16-bit rounding of the weights depends on each shard's running max, so O
-    agrees to about 2^-9 of its scale; lse is computed from fp32 weights."""
+    agrees to within the bf16 weight rounding (at most 2^-8 relative per
+    weight, far less on average over 4000 keys); lse is computed from fp32
+    weights."""
     q, k, v = synth.decode_inputs(1, 8, 2, 4000, 128, "bf16", seed=13, device=DEV)
     outs = [fa.decode(q, k, v, nsplit=n, return_lse=True) for n in (1, 2, 16, 4000)]
     torch.cuda.synchronize()
