@@ -3,13 +3,16 @@ flash-decode, hand-written HIP kernels for gfx950.
 
 This module is the Python binding of libfa_amd.so (C ABI in include/fa.h).
 It only marshals arguments: it checks tensor shapes, dtypes and devices,
-allocates outputs with torch (device memory and streams are all torch is
-used for) and calls the library.  Every step of the computation runs in the
+allocates outputs and workspaces with torch (device memory and streams are
+all torch is used for) and calls the library.  Anything allocated here is
+allocated on the stream the call is launched on, so torch's caching
+allocator cannot hand it to other work before the kernels are done with it.  Every step of the computation runs in the
 library's kernels; if the library is missing the calls raise instead of
 falling back to anything else.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import re
@@ -17,7 +20,8 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "decode", "decode_paged", "decode_workspace_bytes", "lib", "FAError", "LIB_PATH",
+__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "bwd", "bwd_varlen", "bwd_workspace_bytes", "decode",
+           "decode_paged", "decode_workspace_bytes", "lib", "FAError", "LIB_PATH",
            "HEADER_PATH", "status_string"]
 
 LIB_PATH = Path(__file__).resolve().parent / "libfa_amd.so"
@@ -99,6 +103,19 @@ def _need(cond, msg):
         raise ValueError(msg)
 
 
+def _alloc_on(stream):
+    """Context in which torch allocations belong to the launch stream: a
+    buffer freed when the binding returns is then reused only by later work
+    on that same stream, which runs after the kernels that use it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _check_out(t, shape, device, what):
+    _need(t.shape == tuple(shape) and t.dtype == torch.float32 and t.is_contiguous()
+          and t.device == device, f"{what} must be a contiguous fp32 {list(shape)} tensor on {device}")
+
+
+
 def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
         return_lse: bool = True, stream=None):
     """Exact attention forward.  q, k, v: [B, H, N, d] bf16/fp16 CUDA tensors.
@@ -110,15 +127,14 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
-    _need(out.shape == q.shape and out.dtype == torch.float32 and out.is_contiguous()
-          and out.device == q.device, "out must be a contiguous fp32 [B,H,N,d] tensor")
-    if lse is None and return_lse:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with _alloc_on(stream):
+        if out is None:
+            out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+        if lse is None and return_lse:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_out(out, (B, H, N, d), q.device, "out")
     if lse is not None:
-        _need(lse.shape == (B, H, N) and lse.dtype == torch.float32 and lse.is_contiguous()
-              and lse.device == q.device, "lse must be a contiguous fp32 [B,H,N] tensor")
+        _check_out(lse, (B, H, N), q.device, "lse")
     st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                       int(bool(causal)), float(scale), _stream(stream, q.device), _DTYPE[q.dtype])
     _check(st, "fa_fwd")
@@ -136,19 +152,21 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, *, causal: bool = False,
     _need(q.dtype in _DTYPE and q.dtype == k.dtype == v.dtype, "q, k, v must all be bf16 or fp16")
     _need(cu_seqlens.dim() == 1 and cu_seqlens.dtype == torch.int32 and cu_seqlens.numel() >= 1,
           "cu_seqlens must be int32 [B+1]")
+    _need(q.is_cuda and q.is_contiguous(), "q must be a contiguous GPU tensor")
     for t in (k, v, cu_seqlens):
         _need(t.device == q.device and t.is_contiguous(), "contiguous tensors on one GPU")
-    _need(q.is_cuda and q.is_contiguous(), "q must be a contiguous GPU tensor")
     T, H, d = q.shape
     B = cu_seqlens.numel() - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((T, H, d), dtype=torch.float32, device=q.device)
-    _need(out.shape == q.shape and out.dtype == torch.float32 and out.is_contiguous(),
-          "out must be a contiguous fp32 [T,H,d] tensor")
-    if lse is None and return_lse:
-        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    with _alloc_on(stream):
+        if out is None:
+            out = torch.empty((T, H, d), dtype=torch.float32, device=q.device)
+        if lse is None and return_lse:
+            lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    _check_out(out, (T, H, d), q.device, "out")
+    if lse is not None:
+        _check_out(lse, (H, T), q.device, "lse")
     st = lib().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
                              B, H, T, int(max_seqlen), d, int(bool(causal)), float(scale),
                              _stream(stream, q.device), _DTYPE[q.dtype])
@@ -171,15 +189,14 @@ def fwd_fp8(q, k, v, *, q_descale: float, k_descale: float, v_descale: float,
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
-    _need(out.shape == q.shape and out.dtype == torch.float32 and out.is_contiguous()
-          and out.device == q.device, "out must be a contiguous fp32 [B,H,N,d] tensor")
-    if lse is None and return_lse:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with _alloc_on(stream):
+        if out is None:
+            out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+        if lse is None and return_lse:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_out(out, (B, H, N, d), q.device, "out")
     if lse is not None:
-        _need(lse.shape == (B, H, N) and lse.dtype == torch.float32 and lse.is_contiguous()
-              and lse.device == q.device, "lse must be a contiguous fp32 [B,H,N] tensor")
+        _check_out(lse, (B, H, N), q.device, "lse")
     st = lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                           int(bool(causal)), float(scale), float(q_descale), float(k_descale),
                           float(v_descale), _stream(stream, q.device))
@@ -189,6 +206,26 @@ def fwd_fp8(q, k, v, *, q_descale: float, k_descale: float, v_descale: float,
 
 def bwd_workspace_bytes(B: int, H: int, N: int) -> int:
     return int(lib().fa_bwd_workspace_bytes(B, H, N))
+
+
+def _grads(shape, device, given, stream):
+    outs = []
+    with _alloc_on(stream):
+        for g in given:
+            if g is None:
+                g = torch.empty(shape, dtype=torch.float32, device=device)
+            _check_out(g, shape, device, "gradients")
+            outs.append(g)
+    return outs
+
+
+def _workspace(workspace, nbytes, device, stream):
+    if workspace is None:
+        with _alloc_on(stream):
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    _need(workspace.is_cuda and workspace.device == device and workspace.is_contiguous(),
+          "workspace must be a contiguous tensor on the inputs' GPU")
+    return workspace, workspace.numel() * workspace.element_size()
 
 
 def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = None,
@@ -209,20 +246,11 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = No
     _need(all(t.is_contiguous() for t in ts), "tensors must be contiguous")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    outs = []
-    for g in (dq, dk, dv):
-        if g is None:
-            g = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
-        _need(g.shape == q.shape and g.dtype == torch.float32 and g.is_contiguous()
-              and g.device == q.device, "gradients must be contiguous fp32 [B,H,N,d] tensors")
-        outs.append(g)
-    if workspace is None:
-        workspace = torch.empty(max(bwd_workspace_bytes(B, H, N), 1), dtype=torch.uint8,
-                                device=q.device)
+    outs = _grads((B, H, N, d), q.device, (dq, dk, dv), stream)
+    workspace, ws_bytes = _workspace(workspace, bwd_workspace_bytes(B, H, N), q.device, stream)
     st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(outs[0]),
                       _ptr(outs[1]), _ptr(outs[2]), B, H, N, d, int(bool(causal)), float(scale),
-                      _stream(stream, q.device), _DTYPE[q.dtype], _ptr(workspace),
-                      workspace.numel() * workspace.element_size())
+                      _stream(stream, q.device), _DTYPE[q.dtype], _ptr(workspace), ws_bytes)
     _check(st, "fa_bwd")
     return tuple(outs)
 
@@ -248,27 +276,31 @@ def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, *, causal: bo
     B = cu_seqlens.numel() - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    outs = []
-    for g in (dq, dk, dv):
-        if g is None:
-            g = torch.empty((T, H, d), dtype=torch.float32, device=q.device)
-        _need(g.shape == q.shape and g.dtype == torch.float32 and g.is_contiguous()
-              and g.device == q.device, "gradients must be contiguous fp32 [T,H,d] tensors")
-        outs.append(g)
-    if workspace is None:
-        workspace = torch.empty(max(bwd_workspace_bytes(1, H, T), 1), dtype=torch.uint8,
-                                device=q.device)
+    outs = _grads((T, H, d), q.device, (dq, dk, dv), stream)
+    workspace, ws_bytes = _workspace(workspace, bwd_workspace_bytes(1, H, T), q.device, stream)
     st = lib().fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                              _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(cu_seqlens), B, H,
                              T, int(max_seqlen), d, int(bool(causal)), float(scale),
                              _stream(stream, q.device), _DTYPE[q.dtype], _ptr(workspace),
-                             workspace.numel() * workspace.element_size())
+                             ws_bytes)
     _check(st, "fa_bwd_varlen")
     return tuple(outs)
 
 
 def decode_workspace_bytes(B: int, Hq: int, d: int, nsplit: int) -> int:
     return int(lib().fa_decode_workspace_bytes(B, Hq, d, nsplit))
+
+
+def _decode_args(q, kcache, vcache):
+    _need(q.dim() == 3 and kcache.dim() == 4 and kcache.shape == vcache.shape,
+          "q must be [B,Hq,d] and the caches [B,Hkv,L,d]")
+    B, Hq, d = q.shape
+    Bk, Hkv, L, dk = kcache.shape
+    _need(Bk == B and dk == d, "batch / head_dim mismatch between q and the caches")
+    _need(q.dtype in _DTYPE and q.dtype == kcache.dtype == vcache.dtype, "bf16 or fp16 inputs")
+    _need(q.is_cuda and kcache.device == q.device and vcache.device == q.device, "one GPU")
+    _need(q.is_contiguous() and kcache.is_contiguous() and vcache.is_contiguous(), "contiguous")
+    return B, Hq, Hkv, L, d
 
 
 def decode(q, kcache, vcache, *, nsplit: int, out=None, lse=None, return_lse: bool = False,
@@ -278,32 +310,25 @@ def decode(q, kcache, vcache, *, nsplit: int, out=None, lse=None, return_lse: bo
     fa_decode_ex (caller-owned workspace, allocated here with torch if not
     given); otherwise through fa_decode (library-managed workspace).
     Returns (o [B, Hq, d] fp32, lse [B, Hq] fp32 or None)."""
-    _need(q.dim() == 3 and kcache.dim() == 4 and kcache.shape == vcache.shape,
-          "q must be [B,Hq,d] and the caches [B,Hkv,L,d]")
-    B, Hq, d = q.shape
-    Bk, Hkv, L, dk = kcache.shape
-    _need(Bk == B and dk == d, "batch / head_dim mismatch between q and the caches")
-    _need(q.dtype in _DTYPE and q.dtype == kcache.dtype == vcache.dtype, "bf16 or fp16 inputs")
-    _need(q.is_cuda and kcache.device == q.device and vcache.device == q.device, "one GPU")
-    _need(q.is_contiguous() and kcache.is_contiguous() and vcache.is_contiguous(), "contiguous")
-    if out is None:
-        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
-    _need(out.shape == (B, Hq, d) and out.dtype == torch.float32 and out.is_contiguous(),
-          "out must be a contiguous fp32 [B,Hq,d] tensor")
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    B, Hq, Hkv, L, d = _decode_args(q, kcache, vcache)
+    with _alloc_on(stream):
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        if lse is None and return_lse:
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check_out(out, (B, Hq, d), q.device, "out")
+    if lse is not None:
+        _check_out(lse, (B, Hq), q.device, "lse")
     s = _stream(stream, q.device)
     if lse is None and workspace is None:
         st = lib().fa_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(out), B, Hq, Hkv, L, d,
                              int(nsplit), s, _DTYPE[q.dtype])
         _check(st, "fa_decode")
         return out, None
-    if workspace is None:
-        nbytes = decode_workspace_bytes(B, Hq, d, max(1, min(int(nsplit), L)))
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    nbytes = decode_workspace_bytes(B, Hq, d, max(1, min(int(nsplit), L)))
+    workspace, ws_bytes = _workspace(workspace, nbytes, q.device, stream)
     st = lib().fa_decode_ex(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(out), _ptr(lse), B, Hq,
-                            Hkv, L, d, int(nsplit), s, _DTYPE[q.dtype], _ptr(workspace),
-                            workspace.numel() * workspace.element_size())
+                            Hkv, L, d, int(nsplit), s, _DTYPE[q.dtype], _ptr(workspace), ws_bytes)
     _check(st, "fa_decode_ex")
     return out, lse
 
@@ -323,20 +348,23 @@ def decode_paged(q, kpages, vpages, block_table, seq_lens, *, nsplit: int, out=N
     _need(block_table.dim() == 2 and block_table.shape[0] == B and block_table.dtype == torch.int32,
           "block_table must be int32 [B, pages_per_seq]")
     _need(seq_lens.shape == (B,) and seq_lens.dtype == torch.int32, "seq_lens must be int32 [B]")
+    _need(q.is_cuda and q.is_contiguous(), "q must be a contiguous GPU tensor")
     for t in (kpages, vpages, block_table, seq_lens):
         _need(t.device == q.device and t.is_contiguous(), "contiguous tensors on one GPU")
-    _need(q.is_cuda and q.is_contiguous(), "q must be a contiguous GPU tensor")
-    if out is None:
-        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        nbytes = decode_workspace_bytes(B, Hq, d, int(nsplit))
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    with _alloc_on(stream):
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        if lse is None and return_lse:
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check_out(out, (B, Hq, d), q.device, "out")
+    if lse is not None:
+        _check_out(lse, (B, Hq), q.device, "lse")
+    workspace, ws_bytes = _workspace(workspace, decode_workspace_bytes(B, Hq, d, int(nsplit)),
+                                     q.device, stream)
     st = lib().fa_decode_paged(_ptr(q), _ptr(kpages), _ptr(vpages), _ptr(block_table),
                                _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, page_size,
                                block_table.shape[1], num_pages, d, int(nsplit),
                                _stream(stream, q.device), _DTYPE[q.dtype], _ptr(workspace),
-                               workspace.numel() * workspace.element_size())
+                               ws_bytes)
     _check(st, "fa_decode_paged")
     return out, lse

@@ -110,3 +110,57 @@ def test_decode_paged_on_side_stream():
     out = on_side_stream(lambda c, s: fa.decode_paged(c[0], c[1], c[2], c[3], c[4], nsplit=4,
                                                       stream=s), [q, kp, vp, table, lens])
     same(out, ref)
+
+
+def test_stream_argument_outside_its_context():
+    """stream= given while torch's current stream is another one: the binding
+    must allocate its workspace and outputs on the launch stream.  Right after
+    each call the current stream allocates same-sized buffers and overwrites
+    them; if the binding had freed its workspace into the current stream's
+    pool, those writes would land in it while the kernels still use it."""
+    print("case streams: stream argument without entering its context", flush=True)
+    q, kc, vc = synth.decode_inputs(8, 32, 8, 16384, 128, "bf16", seed=4500, device=DEV)
+    ref = fa.decode(q, kc, vc, nsplit=16, return_lse=True)
+    qb, kb, vb, do = synth.bwd_inputs(2, 8, 1024, 128, "bf16", seed=4501, device=DEV)
+    o, lse = fa.fwd(qb, kb, vb)
+    ref_g = fa.bwd(qb, kb, vb, o, lse, do)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(device=DEV)
+    dec_ws = fa.decode_workspace_bytes(8, 32, 128, 16)
+    bwd_ws = fa.bwd_workspace_bytes(2, 8, 1024)
+    for _ in range(3):
+        out = fa.decode(q, kc, vc, nsplit=16, return_lse=True, stream=s)
+        junk = [torch.empty(dec_ws, dtype=torch.uint8, device=DEV).fill_(0x7f) for _ in range(4)]
+        g = fa.bwd(qb, kb, vb, o, lse, do, stream=s)
+        junk += [torch.empty(bwd_ws, dtype=torch.uint8, device=DEV).fill_(0x7f) for _ in range(4)]
+        s.synchronize()
+        torch.cuda.synchronize()
+        same(out, ref)
+        same(g, ref_g)
+        del junk
+
+
+def test_binding_rejects_bad_output_buffers():
+    """Caller-supplied out/lse buffers are checked before any launch."""
+    print("case binding rejects bad out/lse", flush=True)
+    lens = [100, 28]
+    q, k, v, cu = synth.varlen_inputs(lens, 2, 64, "bf16", seed=4600, device=DEV)
+    T = sum(lens)
+    with pytest.raises(ValueError):
+        fa.fwd_varlen(q, k, v, cu, 100, out=torch.empty(T, 2, 64, device=DEV).half())
+    with pytest.raises(ValueError):
+        fa.fwd_varlen(q, k, v, cu, 100, lse=torch.empty(T, 2, device=DEV))      # must be [H, T]
+    with pytest.raises(ValueError):
+        fa.fwd_varlen(q, k, v, cu, 100, out=torch.empty(T, 2, 64))               # host memory
+    qd, kc, vc = synth.decode_inputs(2, 4, 2, 50, 64, "bf16", seed=4601, device=DEV)
+    with pytest.raises(ValueError):
+        fa.decode(qd, kc, vc, nsplit=2, lse=torch.empty(2, 3, device=DEV))
+    with pytest.raises(ValueError):
+        fa.decode(qd, kc, vc, nsplit=2, out=torch.empty(2, 4, 64))
+    kp = synth.normal((4, 16, 2, 64), 4602, "bf16", DEV)
+    table = torch.zeros(2, 2, dtype=torch.int32, device=DEV)
+    seq = torch.full((2,), 20, dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        fa.decode_paged(qd, kp, kp, table, seq, nsplit=2, out=torch.empty(2, 4, 65, device=DEV))
+    with pytest.raises(ValueError):
+        fa.decode_paged(qd, kp, kp, table, seq, nsplit=2, lse=torch.empty(2, 4))
