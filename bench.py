@@ -51,6 +51,9 @@ PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA (256 CU x 8192 flop/clk x 
 FWD = dict(B=8, H=32, N=8192, d=128, dtype="fp16", causal=False, seed=1002)
 DEC = dict(B=8, Hq=32, Hkv=8, L=32768, d=128, dtype="bf16", nsplit=16, seed=1005)
 KV_COPIES = 4                 # decode rotates among this many caches (4 GiB > 256 MB MALL)
+# Untimed warm-up calls of the legs after the step (the FP8 leg uses
+# max(FP8_MIN_WARMUP, --warmup // 2)); --trace-summary skips the same calls.
+FP8_MIN_WARMUP, BWD_WARMUP, VARLEN_WARMUP, PAGED_WARMUP = 5, 3, 3, 5
 
 
 def fwd_flops(B, H, N, d, causal):
@@ -86,6 +89,218 @@ def load_traffic(kernel_key, digest, launches_per_unit=1):
     if not rec or rec.get("source_digest") != digest:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+class ClockPowerSampler:
+    """Samples the GPU's graphics clock and socket power during a timed
+    region, on a background thread, through AMD SMI's library (GPU metrics
+    table: the current clock of every XCD, current socket power, hotspot
+    temperature).  The handle is matched to the torch device by PCI address.
+    If the library or the metrics are unavailable the summary says why."""
+
+    def __init__(self, device, period_s=0.005):
+        self.period, self.samples, self.error, self._h = period_s, [], None, None
+        try:
+            import threading
+            import torch
+            sys.path.append("/opt/rocm/share/amd_smi")
+            import amdsmi
+            self._smi = amdsmi
+            amdsmi.amdsmi_init()
+            props = torch.cuda.get_device_properties(device)
+            want = (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+            for h in amdsmi.amdsmi_get_processor_handles():
+                dom, bus, rest = amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self._h = h
+            if self._h is None:
+                raise RuntimeError(f"no AMD SMI handle at PCI {want}")
+            self._stop = threading.Event()
+            self._t = threading.Thread(target=self._run, daemon=True)
+        except Exception as e:       # sampling is a diagnostic; timing goes on without it
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and c > 0]
+        return {"t": time.perf_counter(), "sclk_mhz": clks,
+                "power_w": m.get("current_socket_power"), "hotspot_c": m.get("temperature_hotspot")}
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._h is not None:
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._h is not None:
+            self._stop.set()
+            self._t.join()
+        return False
+
+    def summary(self):
+        import statistics as st
+        if not self.samples:
+            return {"source": None, "samples": 0, "error": self.error or "no samples"}
+
+        def stats(xs):
+            xs = [x for x in xs if isinstance(x, (int, float))]
+            return {"median": st.median(xs), "min": min(xs), "max": max(xs)} if xs else None
+        out = {"source": "amdsmi gpu_metrics (current_gfxclks, current_socket_power)",
+               "samples": len(self.samples), "period_ms": self.period * 1e3,
+               "sclk_mhz": stats([st.mean(x["sclk_mhz"]) for x in self.samples if x["sclk_mhz"]]),
+               "power_w": stats([x["power_w"] for x in self.samples]),
+               "hotspot_c": stats([x["hotspot_c"] for x in self.samples])}
+        if self.error:
+            out["error"] = self.error
+        return out
+
+
+def trace_summary(paths, warmup, steps, fp8_steps, bwd_steps, varlen_steps, paged_steps):
+    """Kernel times from rocprofv3 kernel-trace CSVs of one run of this
+    script with the same step counts: each kernel's launches in start order,
+    the untimed warm-up launches skipped, averaged over the timed ones only
+    (the forward's kernel is also launched once more by the bwd leg, after
+    the step's launches; those and later launches are not counted)."""
+    import csv
+    import statistics as st
+    csv.field_size_limit(1 << 30)
+    launches = {}
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                launches.setdefault(name, []).append((int(r["Start_Timestamp"]),
+                                                      int(r["End_Timestamp"])))
+    fwd = FWD
+    flops = fwd_flops(fwd["B"], fwd["H"], fwd["N"], fwd["d"], fwd["causal"])
+    fp8_warm = max(FP8_MIN_WARMUP, warmup // 2)
+    # (leg, demangled name prefix, launches skipped, launches timed, algorithmic work, peak)
+    legs = [("fwd", "fa::fa_fwd_kernel<fa::FP16, 128, false, false>(", warmup, steps,
+             ("TFLOP/s", flops, PEAK_MFMA_TFLOPS)),
+            ("decode", "fa::fa_decode_split_kernel<fa::BF16x16, 128, false>(", warmup, steps,
+             ("GB/s", decode_bytes(DEC["B"], DEC["Hq"], DEC["Hkv"], DEC["L"], DEC["d"]),
+              PEAK_HBM_GBS)),
+            ("decode", "fa::fa_decode_combine_few_kernel<16>(", warmup, steps, None),
+            ("fp8_fwd", "fa::fa_fwd_fp8_kernel<128, false>(", fp8_warm, fp8_steps,
+             ("TFLOP/s", flops, PEAK_FP8_TFLOPS)),
+            ("bwd", "fa::fa_bwd_dq_kernel<fa::FP16, 128, false, false>(", BWD_WARMUP, bwd_steps,
+             None),
+            ("bwd", "fa::fa_bwd_dkdv_kernel<fa::FP16, 128, false, false>(", BWD_WARMUP, bwd_steps,
+             None),
+            ("varlen_fwd", "fa::fa_fwd_kernel<fa::FP16, 128, false, true>(", VARLEN_WARMUP,
+             varlen_steps, None),
+            ("paged_decode", "fa::fa_decode_split_kernel<fa::BF16x16, 128, true>(", PAGED_WARMUP,
+             paged_steps, ("GB/s", decode_bytes(DEC["B"], DEC["Hq"], DEC["Hkv"], DEC["L"],
+                                                  DEC["d"]), PEAK_HBM_GBS))]
+    out = []
+    for leg, prefix, skip, take, work in legs:
+        hits = sorted(t for name, ts in launches.items()
+                      if name.startswith(prefix) or name.startswith("void " + prefix) for t in ts)
+        timed = [(e - b) / 1e3 for b, e in hits[skip:skip + take]]
+        if not timed:
+            continue
+        rec = {"leg": leg, "kernel": prefix[:-1], "launches_in_trace": len(hits),
+               "skipped": skip, "timed": len(timed), "avg_us": round(st.mean(timed), 2),
+               "median_us": round(st.median(timed), 2), "min_us": round(min(timed), 2),
+               "max_us": round(max(timed), 2)}
+        if work is not None:
+            unit, amount, peak = work
+            rate = amount / (rec["avg_us"] * 1e-6) / (1e12 if unit == "TFLOP/s" else 1e9)
+            rec.update({"achieved": round(rate, 2), "unit": unit, "peak": peak,
+                        "frac": round(rate / peak, 4)})
+            if unit == "TFLOP/s" and peak == PEAK_MFMA_TFLOPS:
+                rec["frac_of_2500"] = round(rate / 2500.0, 4)
+        out.append(rec)
+    return out
+
+
+def ceilings(mfma_ms=10.0, launches=10):
+    """What the chip sustains on each bound resource doing nothing else
+    (libfa_ceiling.so): 32x32x16 16-bit MFMAs in four independent chains on
+    two waves per SIMD, with N(0,1) operands (the attention inputs' values)
+    and with zero operands; and a 4 GiB stream of 16-byte loads, one
+    contiguous chunk per workgroup, with the decode kernel's non-temporal
+    policy and with the default one.  HIP events on the launch stream; the
+    GPU's clock and power sampled during each timed loop.  One JSON line."""
+    import ctypes
+    import torch
+    from flashattention_attention_fa_amd import synth
+
+    path = os.path.join(ROOT, "flashattention_attention_fa_amd", "libfa_ceiling.so")
+    lib = ctypes.CDLL(path)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.fa_ceiling_mfma.argtypes = [P, P, I, I, I, P]
+    lib.fa_ceiling_read.argtypes = [P, ctypes.c_size_t, P, I, I, P]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(call, n):
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        sampler = ClockPowerSampler(dev)
+        with sampler:
+            e0.record(stream)
+            for _ in range(n):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, sampler.summary()
+
+    out = {"ceilings": "MI355X achievable throughput, one resource at a time", "mfma": [],
+           "hbm_read": []}
+    wg = 512                                   # two 4-wave workgroups per CU
+    res = torch.empty(wg * 256, dtype=torch.float32, device=dev)
+    flops_per_iter = wg * 4 * 4 * 32768.0
+    for dtype, data in (("fp16", "N(0,1)"), ("bf16", "N(0,1)"), ("fp16", "zeros")):
+        ops = synth.normal((wg * 256 * 16,), 9000, dtype, dev)
+        if data == "zeros":
+            ops.zero_()
+        code = 1 if dtype == "fp16" else 0
+        probe = 2000
+        ms, _ = timed(lambda: lib.fa_ceiling_mfma(ctypes.c_void_p(ops.data_ptr()),
+                                                  ctypes.c_void_p(res.data_ptr()), wg, probe,
+                                                  code, sp), 2)
+        iters = max(100, int(probe * mfma_ms / max(ms, 1e-3)))
+        ms, smi = timed(lambda: lib.fa_ceiling_mfma(ctypes.c_void_p(ops.data_ptr()),
+                                                    ctypes.c_void_p(res.data_ptr()), wg, iters,
+                                                    code, sp), launches)
+        tf = flops_per_iter * iters / (ms * 1e-3) / 1e12
+        out["mfma"].append({"kernel": f"fa_ceiling_mfma_kernel<{dtype.upper()}>", "dtype": dtype,
+                            "operands": data, "iters": iters, "avg_launch_ms": round(ms, 4),
+                            "achieved": round(tf, 1), "unit": "TFLOP/s",
+                            "peak": PEAK_MFMA_TFLOPS, "frac": round(tf / PEAK_MFMA_TFLOPS, 4),
+                            "clock_power": smi})
+        print(f"ceiling mfma {dtype} {data}: {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.view(torch.int32).fill_(0x3c003c00)
+    for wgs in (1024, 4096):
+        chk = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+        for nt in (1, 0):
+            ms, smi = timed(lambda: lib.fa_ceiling_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                                        ctypes.c_void_p(chk.data_ptr()), wgs, nt,
+                                                        sp), 20)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            out["hbm_read"].append({"kernel": f"fa_ceiling_read_kernel<{'true' if nt else 'false'}>",
+                                    "policy": "non-temporal (sc0 nt)" if nt else "default",
+                                    "workgroups": wgs, "bytes": nbytes,
+                                    "avg_launch_us": round(ms * 1e3, 2), "achieved": round(gbs, 1),
+                                    "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                                    "frac": round(gbs / PEAK_HBM_GBS, 4), "clock_power": smi})
+            print(f"ceiling read wg={wgs} nt={nt}: {gbs:.1f} GB/s", file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(seconds_target=15.0):
@@ -487,6 +702,72 @@ def cpu_baseline_all_configs(oracle_seconds=3.0):
     print(json.dumps(rec), flush=True)
 
 
+def full_check(name, heads=None):
+    """Check one forward workload of synth.CONFIGS against the oracle on
+    every row of every head (or of the first `heads` heads): one fa_fwd
+    call on the GPU, O and lse copied to the host, then the oracle head by
+    head (one progress line per head on stderr).  Prints one JSON line with
+    the errors over all checked rows and the worst single row."""
+    import numpy as np
+    import torch
+    import flashattention_attention_fa_amd as fa
+    from flashattention_attention_fa_amd import synth
+    from oracle import oracle as oracle_mod
+
+    c = synth.CONFIGS[name]
+    if c["kind"] != "fwd":
+        raise SystemExit(f"--full-check takes a forward workload, not {name}")
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    threads = int(os.environ["OMP_NUM_THREADS"])
+    orc = oracle_mod.get()
+    dev = torch.device("cuda:0")
+    B, H, N, d, causal = c["B"], c["H"], c["N"], c["d"], c["causal"]
+    print(f"full check {name}: fa_fwd B{B} H{H} N{N} d{d} {c['dtype']} causal={causal}",
+          file=sys.stderr, flush=True)
+    q, k, v = synth.fwd_inputs(B, H, N, d, c["dtype"], seed=c["seed"], device=dev,
+                               krow_scale=c.get("krow_scale"))
+    scale = 1 / math.sqrt(d)
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    og, lg = o.cpu().numpy(), lse.cpu().numpy()
+    qb, kb, vb = synth.to_bits(q), synth.to_bits(k), synth.to_bits(v)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    pairs = [(b, h) for b in range(B) for h in range(H)][:heads]
+    sq_err = sq_ref = 0.0
+    max_abs = lse_abs = worst_row = 0.0
+    worst_at = None
+    odt = 0.0
+    for n, (b, h) in enumerate(pairs):
+        rows = np.stack([np.full(N, b), np.full(N, h), np.arange(N)], 1).astype(np.int64)
+        t0 = time.perf_counter()
+        ro, rl = orc.attention_rows(qb, kb, vb, c["dtype"], rows, causal, scale)
+        odt += time.perf_counter() - t0
+        diff = og[b, h].astype(np.float64) - ro
+        sq_err += float(np.sum(diff * diff))
+        sq_ref += float(np.sum(ro * ro))
+        head_abs = float(np.abs(diff).max())
+        row_rel = np.linalg.norm(diff, axis=1) / np.maximum(np.linalg.norm(ro, axis=1), 1e-300)
+        i = int(np.argmax(row_rel))
+        if row_rel[i] > worst_row:
+            worst_row, worst_at = float(row_rel[i]), (b, h, i)
+        max_abs = max(max_abs, head_abs)
+        lse_abs = max(lse_abs, float(np.abs(lg[b, h].astype(np.float64) - rl).max()))
+        print(f"head {n + 1}/{len(pairs)} (b={b}, h={h}): max-abs {head_abs:.3e}, so far "
+              f"{max_abs:.3e}, lse {lse_abs:.3e}, oracle {odt:.0f} s", file=sys.stderr, flush=True)
+    rec = {"full_check": name,
+           "shape": f"fwd B{B} H{H} N{N} d{d} {c['dtype']} "
+                    f"{'causal' if causal else 'non-causal'}"
+                    + (" K rows x U[0.5,4]" if c.get("krow_scale") else ""),
+           "heads_checked": len(pairs), "rows_checked": len(pairs) * N,
+           "max_abs": max_abs, "rel_l2": math.sqrt(sq_err / sq_ref), "lse_max_abs": lse_abs,
+           "worst_row_rel_l2": worst_row, "worst_row": worst_at,
+           "bars": {"max_abs": 2e-2, "rel_l2": 5e-3, "lse_max_abs": 1e-3},
+           "oracle": {"seconds": round(odt, 1), "cores": threads}}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -511,13 +792,36 @@ def main():
                          "key-scaled causal, 128k causal, decode, varlen batch, paged decode) "
                          "with its oracle time and parity on the oracle's rows, one JSON line "
                          "each")
+    ap.add_argument("--full-check", metavar="WORKLOAD", default=None,
+                    help="instead of the step: check one forward workload (e.g. "
+                         "causal_b4h32n16k_kscaled) against the oracle on every row")
+    ap.add_argument("--heads", type=int, default=None,
+                    help="with --full-check: check only the first HEADS heads")
+    ap.add_argument("--trace-summary", nargs="+", metavar="CSV", default=None,
+                    help="instead of running: per-kernel times over the timed launches only, from "
+                         "rocprofv3 kernel-trace CSVs of a run of this script with the same "
+                         "--steps/--warmup/leg-step options (one JSON line per kernel)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="instead of the step: the achievable MFMA and HBM-read ceilings "
+                         "(libfa_ceiling.so), with clock and power")
     args = ap.parse_args()
+    if args.trace_summary:
+        for rec in trace_summary(args.trace_summary, args.warmup, args.steps, args.fp8_steps,
+                                 args.bwd_steps, args.varlen_steps, args.paged_steps):
+            print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     if args.all_configs:
         cpu_baseline_all_configs()
+        return
+    if args.full_check:
+        full_check(args.full_check, args.heads)
+        return
+    if args.ceilings:
+        ceilings()
         return
 
     import torch
@@ -574,16 +878,22 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
-    dec_ms = sum(b.elapsed_time(e) for _, b, e in ev) / args.steps
+    sampler = ClockPowerSampler(dev)
+    with sampler:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            step(i)
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    fwd_calls = [a.elapsed_time(b) for a, b, _ in ev]
+    dec_calls = [b.elapsed_time(e) for _, b, e in ev]
+    fwd_ms = sum(fwd_calls) / args.steps
+    dec_ms = sum(dec_calls) / args.steps
     step_ms = sum(a.elapsed_time(e) for a, _, e in ev) / args.steps
+    median = lambda xs: sorted(xs)[len(xs) // 2] if len(xs) % 2 else \
+        0.5 * (sorted(xs)[len(xs) // 2 - 1] + sorted(xs)[len(xs) // 2])
 
     flops = fwd_flops(c["B"], c["H"], c["N"], c["d"], c["causal"])
     tflops = flops / (fwd_ms * 1e-3) / 1e12 if run_fwd else 0.0
@@ -626,6 +936,7 @@ def main():
             "algorithmic_flops_per_launch": flops,
             "algorithmic_bytes_per_launch": fwd_bytes(c["B"], c["H"], c["N"], c["d"]),
             "avg_launch_ms": round(fwd_ms, 4),
+            "median_launch_ms": round(median(fwd_calls), 4),
             "source_digest": fwd_digest,
         },
         "decode": {
@@ -638,20 +949,23 @@ def main():
             "traffic": dec_traffic,
             "algorithmic_bytes_per_call": dbytes,
             "avg_call_us": round(dec_ms * 1e3, 2),
+            "median_call_us": round(median(dec_calls) * 1e3, 2),
             "kv_cache_copies_rotated": KV_COPIES,
             "source_digest": dec_digest,
         },
         "wall_s_timed": round(wall, 3),
+        "clock_power": sampler.summary(),
         "device": torch.cuda.get_device_name(dev),
     }
     if args.fp8_steps > 0 and args.only is None:
-        out["fp8_fwd"] = time_fp8(fa, synth, stream, args.fp8_steps, max(5, args.warmup // 2))
+        out["fp8_fwd"] = time_fp8(fa, synth, stream, args.fp8_steps,
+                                  max(FP8_MIN_WARMUP, args.warmup // 2))
     if args.bwd_steps > 0 and args.only is None:
-        out["bwd"] = time_bwd(fa, synth, stream, args.bwd_steps, 3)
+        out["bwd"] = time_bwd(fa, synth, stream, args.bwd_steps, BWD_WARMUP)
     if args.varlen_steps > 0 and args.only is None:
-        out["varlen_fwd"] = time_varlen(fa, synth, stream, args.varlen_steps, 3)
+        out["varlen_fwd"] = time_varlen(fa, synth, stream, args.varlen_steps, VARLEN_WARMUP)
     if args.paged_steps > 0 and args.only is None:
-        out["paged_decode"] = time_paged(fa, synth, stream, args.paged_steps, 5)
+        out["paged_decode"] = time_paged(fa, synth, stream, args.paged_steps, PAGED_WARMUP)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

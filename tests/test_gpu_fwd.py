@@ -69,6 +69,19 @@ def test_causal_kscaled_sampled(orc):
     run_rows(orc, c, rows)
 
 
+def test_causal_kscaled_full_heads(orc):
+    """Eight complete heads (131072 rows, every row of each) of the key-scaled
+    causal workload: the workload whose rows are the most peaked (a few keys
+    scaled up to 4x dominate them), so the rounding of a dominant weight
+    shows here first.  Heads spread over all four batches."""
+    c = synth.CONFIGS["causal_b4h32n16k_kscaled"]
+    heads = [(0, 5), (0, 11), (0, 24), (1, 0), (1, 17), (2, 9), (2, 30), (3, 21)]
+    N = c["N"]
+    rows = np.concatenate([np.stack([np.full(N, b), np.full(N, h), np.arange(N)], 1)
+                           for b, h in heads]).astype(np.int64)
+    run_rows(orc, c, rows)
+
+
 def test_long_causal_sampled(orc):
     c = synth.CONFIGS["causal_b1h32n128k"]
     rows = synth.boundary_rows(c["B"], c["H"], c["N"], seed=c["seed"], n_random=64)
