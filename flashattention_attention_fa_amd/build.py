@@ -1,6 +1,8 @@
 """Build libfa_amd.so (the C ABI of include/fa.h) from csrc/ with hipcc for
-gfx950.  Objects go to _build/ at the repository root; the shared library is
-written next to this file, where the Python binding loads it."""
+gfx950, and libfa_ceiling.so (include/fa_ceiling.h: the measurement kernels
+the benchmark's --ceilings mode runs).  Objects go to _build/ at the
+repository root; the shared libraries are written next to this file, where
+the Python binding and the benchmark load them."""
 from __future__ import annotations
 
 import os
@@ -13,6 +15,8 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libfa_amd.so"
+CEILING_LIB = PKG / "libfa_ceiling.so"
+CEILING_SOURCES = ["fa_ceiling.hip"]
 BUILD_DIR = ROOT / "_build"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -51,12 +55,14 @@ def build(verbose: bool = False, resource_report: bool = False) -> Path:
              verbose or resource_report)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB.with_name(f"{LIB.name}.tmp{os.getpid():x}")
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", str(tmp),
-          *map(str, objs), "-Wl,-rpath,/opt/rocm/lib"], verbose)
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(CEILING_SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + CEILING_SOURCES))
+    for lib, names in ((LIB, SOURCES), (CEILING_LIB, CEILING_SOURCES)):
+        tmp = lib.with_name(f"{lib.name}.tmp{os.getpid():x}")
+        _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", str(tmp),
+              *(str(o) for o, n in zip(objs, SOURCES + CEILING_SOURCES) if n in names),
+              "-Wl,-rpath,/opt/rocm/lib"], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -1,0 +1,99 @@
+// fa_ceiling.hip -- measurement kernels of libfa_ceiling.so (include/fa_ceiling.h):
+// the matrix-core throughput and the HBM read bandwidth that gfx950 sustains
+// when doing nothing else, the achievable ceilings against which the
+// attention kernels' own rates can be read.
+#include "fa_ceiling.h"
+#include "fa_device.hpp"
+
+namespace fa {
+
+// Every wave runs four independent accumulation chains of 32x32x16 MFMAs on
+// operands loaded once: the matrix core never waits for a previous result
+// (three other products issue in between) and nothing else is issued in the
+// loop but the loop counter.  Two workgroups of four waves per CU put two
+// waves on every SIMD, as the forward kernel does.
+template <typename T>
+__global__ __launch_bounds__(256, 2) void fa_ceiling_mfma_kernel(const u32x4 *__restrict__ ops,
+                                                                  float *__restrict__ out,
+                                                                  int iters) {
+    typedef typename T::vec8 vec8;
+    const size_t lane = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const vec8 a = as_vec8<vec8>(ops[2 * lane]);
+    const vec8 b = as_vec8<vec8>(ops[2 * lane + 1]);
+    floatx16 c0, c1, c2, c3;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c0[r] = c1[r] = c2[r] = c3[r] = 0.f;
+    for (int i = 0; i < iters; ++i) {
+        c0 = T::mfma32(a, b, c0);
+        c1 = T::mfma32(b, a, c1);
+        c2 = T::mfma32(a, a, c2);
+        c3 = T::mfma32(b, b, c3);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += (c0[r] + c1[r]) + (c2[r] + c3[r]);
+    out[lane] = s;
+}
+
+// Each workgroup streams one contiguous chunk of the buffer, as a decode
+// workgroup streams its shard of the cache: 256 lanes x 16 bytes per load,
+// four loads in flight per lane, through a buffer resource over the chunk
+// (loads past its end return zero), folded into an XOR so that no load can
+// be dropped.  STREAM selects the decode kernel's non-temporal policy.
+template <bool STREAM>
+__global__ __launch_bounds__(256) void fa_ceiling_read_kernel(const unsigned char *__restrict__ src,
+                                                              size_t bytes, uint32_t chunk,
+                                                              unsigned *__restrict__ out) {
+    const size_t start = (size_t)blockIdx.x * chunk;
+    const uint32_t n = start < bytes ? (uint32_t)min((size_t)chunk, bytes - start) : 0u;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc_uniform(src + start, n);
+    auto load = [&](uint32_t off) __attribute__((always_inline)) {
+        return STREAM ? buffer_load16_stream(r, off) : buffer_load16(r, off);
+    };
+    u32x4 x = zero4();
+    for (uint32_t off = threadIdx.x * 16u; off < n; off += 4u * 4096u) {
+        const u32x4 a = load(off), b = load(off + 4096u), c = load(off + 8192u),
+                    d = load(off + 12288u);
+        x ^= (a ^ b) ^ (c ^ d);
+    }
+    out[(size_t)blockIdx.x * 256 + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
+}
+
+}  // namespace fa
+
+extern "C" {
+
+int fa_ceiling_mfma(const void *operands, float *out, int workgroups, int iters, int dtype,
+                    hipStream_t stream) {
+    if (!operands || !out || workgroups < 1 || iters < 1 || (dtype != 0 && dtype != 1) ||
+        (reinterpret_cast<uintptr_t>(operands) & 15))
+        return (int)hipErrorInvalidValue;
+    const fa::u32x4 *ops = static_cast<const fa::u32x4 *>(operands);
+    if (dtype == 1)
+        hipLaunchKernelGGL(fa::fa_ceiling_mfma_kernel<fa::FP16>, dim3(workgroups), dim3(256), 0,
+                           stream, ops, out, iters);
+    else
+        hipLaunchKernelGGL(fa::fa_ceiling_mfma_kernel<fa::BF16>, dim3(workgroups), dim3(256), 0,
+                           stream, ops, out, iters);
+    return (int)hipGetLastError();
+}
+
+int fa_ceiling_read(const void *src, size_t bytes, unsigned *out, int workgroups,
+                    int nontemporal, hipStream_t stream) {
+    if (!src || !out || workgroups < 1 || bytes == 0 || (bytes & 15) ||
+        (reinterpret_cast<uintptr_t>(src) & 15))
+        return (int)hipErrorInvalidValue;
+    // chunk: bytes / workgroups rounded up to 16 KiB (one round of four loads)
+    const size_t chunk = ((bytes + workgroups - 1) / workgroups + 16383) / 16384 * 16384;
+    if (chunk >= (size_t(1) << 31)) return (int)hipErrorInvalidValue;
+    const unsigned char *p = static_cast<const unsigned char *>(src);
+    if (nontemporal)
+        hipLaunchKernelGGL(fa::fa_ceiling_read_kernel<true>, dim3(workgroups), dim3(256), 0,
+                           stream, p, bytes, (uint32_t)chunk, out);
+    else
+        hipLaunchKernelGGL(fa::fa_ceiling_read_kernel<false>, dim3(workgroups), dim3(256), 0,
+                           stream, p, bytes, (uint32_t)chunk, out);
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"

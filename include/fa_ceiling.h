@@ -1,0 +1,58 @@
+/*
+ * fa_ceiling.h -- C ABI of libfa_ceiling.so: two measurement kernels that
+ * show what MI355X (gfx950) sustains on the two resources the attention
+ * kernels of libfa_amd.so are bound by, so that their roofline fractions can
+ * be read against an achievable ceiling as well as the published peak.
+ * Nothing here is part of the attention path.
+ *
+ *  - The matrix-core ceiling: waves that do nothing but 32x32x16 16-bit
+ *    MFMAs (the instruction both products of the forward use) on operands
+ *    taken from memory once, so the values the matrix cores multiply have
+ *    the statistics of real inputs (power draw depends on them).
+ *  - The HBM read ceiling: a grid-stride stream of 16-byte loads over a
+ *    buffer much larger than the last-level cache, with the non-temporal
+ *    policy the decode kernel uses, or the default one.
+ *
+ * Both enqueue on `stream` and return hipSuccess (0) or the HIP error of the
+ * launch; arguments are checked first (hipErrorInvalidValue, nothing
+ * enqueued).  All pointers are device pointers owned by the caller.
+ */
+#ifndef FA_AMD_FA_CEILING_H
+#define FA_AMD_FA_CEILING_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * fa_ceiling_mfma -- `workgroups` workgroups of 4 waves; every wave issues
+ * iters x 4 MFMAs v_mfma_f32_32x32x16_{bf16 (dtype 0), f16 (dtype 1)} in four
+ * independent accumulation chains, i.e. 4 * 32768 * iters flops per wave.
+ *   operands : workgroups * 256 lanes * 16 16-bit values (each lane's A and
+ *              B operand), 16-byte aligned
+ *   out      : workgroups * 256 floats (a checksum per lane, written)
+ *   workgroups >= 1, iters >= 1, dtype 0 or 1
+ */
+int fa_ceiling_mfma(const void *operands, float *out, int workgroups, int iters, int dtype,
+                    hipStream_t stream);
+
+/*
+ * fa_ceiling_read -- reads `bytes` bytes of `src` once, 16 bytes per load:
+ * workgroup w of `workgroups` (256 lanes each) streams the w-th contiguous
+ * chunk of ceil(bytes / workgroups) bytes rounded up to 16 KiB;
+ * nontemporal != 0 gives the loads the decode kernel's streaming
+ * (non-temporal) cache policy.
+ *   src : 16-byte aligned, bytes a positive multiple of 16, chunk < 2 GiB
+ *   out : workgroups * 256 uint32 (an XOR checksum per lane, written)
+ */
+int fa_ceiling_read(const void *src, size_t bytes, unsigned *out, int workgroups,
+                    int nontemporal, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_AMD_FA_CEILING_H */

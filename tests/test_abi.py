@@ -260,3 +260,29 @@ def test_python_binding_rejects_bad_tensors():
         fa.bwd_varlen(p, p, p, torch.zeros(16, 2, 64), torch.zeros(16, 2), p, cu, 16)
     with pytest.raises(ValueError):      # cu_seqlens must be int32
         fa.bwd_varlen(p, p, p, torch.zeros(16, 2, 64), torch.zeros(2, 16), p, cu.long(), 16)
+
+
+def test_ceiling_library_exports_and_rejects():
+    """libfa_ceiling.so (the benchmark's measurement kernels) exports what
+    include/fa_ceiling.h declares and rejects bad arguments before any launch."""
+    import re
+    from pathlib import Path
+    path = Path(fa.LIB_PATH).with_name("libfa_ceiling.so")
+    C = ctypes.CDLL(str(path))
+    text = re.sub(r"/\*.*?\*/", "", (Path(fa.HEADER_PATH).with_name("fa_ceiling.h")).read_text(),
+                  flags=re.S)
+    names = re.findall(r"^\s*int\s+(fa_[a-z0-9_]+)\s*\(", text, flags=re.M)
+    assert names == ["fa_ceiling_mfma", "fa_ceiling_read"]
+    for n in names:
+        assert hasattr(C, n), n
+    P, I = ctypes.c_void_p, ctypes.c_int
+    C.fa_ceiling_mfma.argtypes = [P, P, I, I, I, P]
+    C.fa_ceiling_read.argtypes = [P, ctypes.c_size_t, P, I, I, P]
+    bad = 1                                               # hipErrorInvalidValue
+    assert C.fa_ceiling_mfma(None, A, 1, 1, 1, None) == bad
+    assert C.fa_ceiling_mfma(A, A, 0, 1, 1, None) == bad
+    assert C.fa_ceiling_mfma(A, A, 1, 1, 2, None) == bad
+    assert C.fa_ceiling_mfma(MIS, A, 1, 1, 1, None) == bad
+    assert C.fa_ceiling_read(A, 0, A, 1, 1, None) == bad
+    assert C.fa_ceiling_read(A, 24, A, 1, 1, None) == bad
+    assert C.fa_ceiling_read(A, 1 << 32, A, 1, 1, None) == bad    # a 4 GiB chunk
