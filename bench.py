@@ -95,8 +95,11 @@ class ClockPowerSampler:
     """Samples the GPU's graphics clock and socket power during a timed
     region, on a background thread, through AMD SMI's library (GPU metrics
     table: the current clock of every XCD, current socket power, hotspot
-    temperature).  The handle is matched to the torch device by PCI address.
-    If the library or the metrics are unavailable the summary says why."""
+    temperature).  The table is refreshed about once a second, so a
+    window needs a few seconds to hold several readings; readings are told
+    apart by the table's own system clock counter.  The handle is matched
+    to the torch device by PCI address.  If the library or the metrics are
+    unavailable the summary says why."""
 
     def __init__(self, device, period_s=0.005):
         self.period, self.samples, self.error, self._h = period_s, [], None, None
@@ -122,8 +125,8 @@ class ClockPowerSampler:
 
     def _read(self):
         m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
-        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and c > 0]
-        return {"t": time.perf_counter(), "sclk_mhz": clks,
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and 0 < c < 65535]
+        return {"t": time.perf_counter(), "stamp": m.get("system_clock_counter"), "sclk_mhz": clks,
                 "power_w": m.get("current_socket_power"), "hotspot_c": m.get("temperature_hotspot")}
 
     def _run(self):
@@ -137,6 +140,7 @@ class ClockPowerSampler:
 
     def __enter__(self):
         if self._h is not None:
+            self.t0 = time.perf_counter()
             self._t.start()
         return self
 
@@ -144,21 +148,34 @@ class ClockPowerSampler:
         if self._h is not None:
             self._stop.set()
             self._t.join()
+            self.t1 = time.perf_counter()
         return False
 
     def summary(self):
         import statistics as st
-        if not self.samples:
-            return {"source": None, "samples": 0, "error": self.error or "no samples"}
+        # one reading per refresh of the metrics table; the first one was
+        # taken before the window began
+        seen, reads = set(), []
+        for x in self.samples:
+            if x["stamp"] not in seen:
+                seen.add(x["stamp"])
+                reads.append(x)
+        reads = reads[1:]
+        if not reads:
+            return {"source": None if not self.samples else "amdsmi gpu_metrics",
+                    "readings": 0, "samples": len(self.samples),
+                    "error": self.error or "no refresh of the metrics table inside the window"}
 
         def stats(xs):
             xs = [x for x in xs if isinstance(x, (int, float))]
             return {"median": st.median(xs), "min": min(xs), "max": max(xs)} if xs else None
-        out = {"source": "amdsmi gpu_metrics (current_gfxclks, current_socket_power)",
-               "samples": len(self.samples), "period_ms": self.period * 1e3,
-               "sclk_mhz": stats([st.mean(x["sclk_mhz"]) for x in self.samples if x["sclk_mhz"]]),
-               "power_w": stats([x["power_w"] for x in self.samples]),
-               "hotspot_c": stats([x["hotspot_c"] for x in self.samples])}
+        out = {"source": "amdsmi gpu_metrics (current_gfxclks mean over XCDs, "
+                         "current_socket_power), refreshed about once a second",
+               "window_s": round(self.t1 - self.t0, 2), "readings": len(reads),
+               "sclk_mhz": stats([st.mean(x["sclk_mhz"]) for x in reads if x["sclk_mhz"]]),
+               "sclk_mhz_per_xcd_last": reads[-1]["sclk_mhz"],
+               "power_w": stats([x["power_w"] for x in reads]),
+               "hotspot_c": stats([x["hotspot_c"] for x in reads])}
         if self.error:
             out["error"] = self.error
         return out
@@ -244,18 +261,25 @@ def ceilings(mfma_ms=10.0, launches=10):
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
 
-    def timed(call, n):
+    def timed(call, n, window_s=3.0):
+        """Average time of n calls; the calls then go on, untimed, until the
+        clock/power window has lasted window_s seconds."""
         for _ in range(3):
             call()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         sampler = ClockPowerSampler(dev)
         with sampler:
+            t0 = time.perf_counter()
             e0.record(stream)
             for _ in range(n):
                 call()
             e1.record(stream)
             torch.cuda.synchronize()
+            while time.perf_counter() - t0 < window_s:
+                for _ in range(8):
+                    call()
+                torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n, sampler.summary()
 
     out = {"ceilings": "MI355X achievable throughput, one resource at a time", "mfma": [],
@@ -271,7 +295,7 @@ def ceilings(mfma_ms=10.0, launches=10):
         probe = 2000
         ms, _ = timed(lambda: lib.fa_ceiling_mfma(ctypes.c_void_p(ops.data_ptr()),
                                                   ctypes.c_void_p(res.data_ptr()), wg, probe,
-                                                  code, sp), 2)
+                                                  code, sp), 2, window_s=0.0)
         iters = max(100, int(probe * mfma_ms / max(ms, 1e-3)))
         ms, smi = timed(lambda: lib.fa_ceiling_mfma(ctypes.c_void_p(ops.data_ptr()),
                                                     ctypes.c_void_p(res.data_ptr()), wg, iters,
@@ -801,6 +825,9 @@ def main():
                     help="instead of running: per-kernel times over the timed launches only, from "
                          "rocprofv3 kernel-trace CSVs of a run of this script with the same "
                          "--steps/--warmup/leg-step options (one JSON line per kernel)")
+    ap.add_argument("--sustain-s", type=float, default=3.0,
+                    help="keep running the step (untimed) until this many seconds after the "
+                         "timed steps began, so the clock/power readings cover several refreshes")
     ap.add_argument("--ceilings", action="store_true",
                     help="instead of the step: the achievable MFMA and HBM-read ceilings "
                          "(libfa_ceiling.so), with clock and power")
@@ -862,16 +889,15 @@ def main():
     run_fwd = args.only in (None, "fwd")
     run_dec = args.only in (None, "decode")
 
-    def step(i):
+    def step(i, mid=None):
         if run_fwd:
             fa.fwd(q, k, v, causal=c["causal"], scale=scale, out=o, lse=lse, stream=stream)
-        if ev is not None:
-            ev[i][1].record(stream)
+        if mid is not None:
+            mid.record(stream)
         if run_dec:
             dq, dk, dv = caches[i % KV_COPIES]
             fa.decode(dq, dk, dv, nsplit=dcfg["nsplit"], out=do, lse=dlse, workspace=ws, stream=stream)
 
-    ev = None
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -883,10 +909,18 @@ def main():
         t0 = time.perf_counter()
         for i in range(args.steps):
             ev[i][0].record(stream)
-            step(i)
+            step(i, ev[i][1])
             ev[i][2].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        # The clock and power readings refresh about once a second: keep the
+        # same step running (untimed) until the window holds a few of them.
+        n_extra = 0
+        while time.perf_counter() - t0 < args.sustain_s:
+            for _ in range(4):
+                step(n_extra)
+                n_extra += 1
+            torch.cuda.synchronize()
     fwd_calls = [a.elapsed_time(b) for a, b, _ in ev]
     dec_calls = [b.elapsed_time(e) for _, b, e in ev]
     fwd_ms = sum(fwd_calls) / args.steps
@@ -954,7 +988,9 @@ def main():
             "source_digest": dec_digest,
         },
         "wall_s_timed": round(wall, 3),
-        "clock_power": sampler.summary(),
+        "clock_power": dict(sampler.summary(),
+                            window=f"the {args.steps} timed steps, then {n_extra} more untimed "
+                                   f"steps up to {args.sustain_s:g} s"),
         "device": torch.cuda.get_device_name(dev),
     }
     if args.fp8_steps > 0 and args.only is None:

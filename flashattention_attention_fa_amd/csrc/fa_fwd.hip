@@ -34,10 +34,10 @@
 //                 (then m, O and l are updated as above and the tile's
 //                 weights recomputed).  Any m that keeps the weights finite
 //                 gives the same O and lse; the bound keeps them small.
-//                 With bf16 weights the bound is tighter: m is also raised
-//                 when a tile's largest weight would carry more than an
-//                 eighth of its lane's running sum, so that a weight which
-//                 dominates its row is exactly 1 (see kLeadShareLog2).
+//                 With bf16 weights the bound is tighter: a tile whose
+//                 weights would more than double a lane's running sum asks
+//                 too, so that a weight which dominates its row is exactly 1
+//                 (see kTileShareBf16).
 //   O^T += V^T P^T  P^T is the S^T accumulator converted to 16 bits in
 //                 place; V^T comes from the row-major V tile through the
 //                 transposing LDS read.
@@ -109,16 +109,15 @@ constexpr float kTileSumLimit = 1024.0f;
 // can move it by 2^-8 of itself (fp16: 2^-11).  A weight of 2^x with x > 0
 // is such a rounded value, and if its key dominates the row's softmax the
 // whole output row inherits that error (up to 2^-8 * |v|).  A weight of
-// exactly 1, the running maximum's own, is exact.  So with bf16 the running
-// max m is raised to the tile's row maximum before the tile's exponentials
-// whenever, in some lane, the tile's largest exponent x = c*s - m exceeds
-// log2(lane's running sum) - kLeadShareLog2, i.e. that weight would be more
-// than 2^-kLeadShareLog2 of the sum so far, or exceeds kMaxLead (every weight
-// then stays at most 2^10, the bound kTileSumLimit gives the fp16 path).  A
-// weight left above 1 thus holds at most a ninth of its row, and random
-// data raises m on a few early tiles per row.
-constexpr float kLeadShareLog2 = 3.0f;
-constexpr float kMaxLead = 10.0f;
+// exactly 1, the running maximum's own, is exact.  So with bf16 a tile's
+// weights are only accepted as they are while in every lane they sum to at
+// most the lane's running sum over the earlier tiles (and to kTileSumLimit);
+// otherwise m is raised to the tile's row maximum if that exceeds m, and the
+// weights are recomputed.  A weight left above 1 thus holds at most half of
+// its row.  On random data this recomputes a tile in the first few tiles of
+// a row only.  (The share is 1: measured against smaller ones, it keeps
+// random rows' recomputes to the first three tiles.)
+constexpr float kTileShareBf16 = 1.0f;
 
 // Packed variable-length batches (VARLEN): q, k, v, o are [T, H, D] with
 // sequence b at rows [cu[b], cu[b+1]); lse is [H, T].
@@ -142,8 +141,8 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     constexpr int BM = C::BM, BN = C::BN, KB = C::KB, KCH = C::KCH;
     constexpr int KSTEPS = D / 16;         // QK^T MFMAs per 32-key block
     constexpr int DB = D / 32;             // 32-dim blocks of O
-    // Exact dominant weights (bf16 storage): see kLeadShareLog2.
-    constexpr bool LEAD = std::is_same<T, BF16>::value;
+    // Dominant weights kept exact (bf16 storage): see kTileShareBf16.
+    constexpr bool SHARE = std::is_same<T, BF16>::value;
 
     // Two K and two V tile buffers, each its own LDS object: every access
     // below names its buffer at compile time, so the compiler can tell that
@@ -334,12 +333,9 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     // from tile 0 on (every query sees key 0), so x never involves an
     // infinite base.  tsum collects this lane's part of the tile's row sum,
     // from the fp32 weights (the 16-bit rounding of P, up to 2^-8 relative
-    // for bf16 and 2^-11 for fp16, stays out of l and lse).  With bf16, xm
-    // collects this lane's largest exponent of the tile next to the shifts.
-    float xm = -INFINITY;
+    // for bf16 and 2^-11 for fp16, stays out of l and lse).
     auto shift = [&](floatx16 (&x)[KB], int kb, int r) __attribute__((always_inline)) {
         x[kb][r] = fmaf(x[kb][r], c, -m_run);
-        if constexpr (LEAD) xm = __builtin_elementwise_maximum(xm, x[kb][r]);
     };
     float tsum = 0.f;
     auto softmax_part = [&](const floatx16 (&x)[KB], int kb, int u) __attribute__((always_inline)) {
@@ -354,10 +350,11 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     // Accept the tile's weights, or (rare) raise m by the tile's largest
     // exponent (to the tile's exact row maximum), rescale O and l, shift the
     // exponents and recompute the weights.  The negated test also catches an
-    // infinite sum.
+    // infinite sum.  bf16 also asks when a lane's tile sum passes its running
+    // sum, and then raises only if the row maximum is above m.
     auto accept = [&](floatx16 (&x)[KB]) __attribute__((always_inline)) {
-        // bf16: lead() has already bounded every weight of the tile by 2^10.
-        if (!LEAD && __any(!(tsum <= kTileSumLimit))) {
+        const float limit = SHARE ? fminf(l_run * kTileShareBf16, kTileSumLimit) : kTileSumLimit;
+        if (__any(!(tsum <= limit))) {
             // Keep this a real branch: the compiler would otherwise turn it
             // into unconditional work on every tile.
             asm volatile("" ::: "memory");
@@ -369,37 +366,7 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
                     mx = __builtin_elementwise_maximum(mx, x[kb][r]);
             // delta >= 0; a lane whose keys are all masked has mx = -inf.
             const float delta = fmaxf(max_halves(mx), 0.f);
-            const float alpha = __builtin_amdgcn_exp2f(-delta);
-            m_run += delta;
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) x[kb][r] -= delta;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) softmax_part(x, kb, u);
-        }
-        l_run += tsum;
-    };
-
-    // bf16, before the exponentials of a tile whose exponents x (and this
-    // lane's largest, xm) the previous phase formed: raise m to the tile's
-    // row maximum if some lane's largest weight would exceed 2^-3 of its
-    // running sum or 2^10 (kLeadShareLog2).  A lane whose keys are all masked
-    // has xm = -inf and never asks; l_run = 0 asks at any x > 0.
-    auto lead = [&](floatx16 (&x)[KB]) __attribute__((always_inline)) {
-        if constexpr (LEAD) {
-            const float thr = __builtin_amdgcn_fmed3f(
-                __builtin_amdgcn_logf(l_run) - kLeadShareLog2, 0.f, kMaxLead);
-            if (__any(xm > thr)) {
-                asm volatile("" ::: "memory");
-                const float delta = fmaxf(max_halves(xm), 0.f);
+            if (!SHARE || __any(delta > 0.f)) {
                 const float alpha = __builtin_amdgcn_exp2f(-delta);
                 m_run += delta;
                 l_run *= alpha;
@@ -411,8 +378,13 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) x[kb][r] -= delta;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) softmax_part(x, kb, u);
             }
         }
+        l_run += tsum;
     };
 
     // Tiles before n_full need no mask for any query of the workgroup: all
@@ -439,7 +411,6 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) shift(sA, kb, r);
-    xm = -INFINITY;   // m is tile 0's exact row maximum
     // Iteration 0 overwrites K0; every wave must be done reading K(0).
     __syncthreads();
 
@@ -462,7 +433,6 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
 
         load_k(j + 2, kb_fill);
         load_v(j + 1, vb_fill);
-        lead(cur);
         // Phase 1: QK^T(j+1) | softmax(j).
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -478,7 +448,6 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
         // Phase 2: PV(j) | mask and exponents of tile j+1, SPM scores next
         // to each of the 2*KB*DB MFMAs.
         if constexpr (MASK_NEXT) mask(nxt, j + 1);
-        xm = -INFINITY;
         constexpr int SPM = 16 * KB / (2 * KB * DB);
         static_assert(SPM * 2 * KB * DB == 16 * KB, "phase 2 must cover every score once");
 #pragma unroll
@@ -513,7 +482,6 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
 
     // Last tile: softmax and PV only.
     auto last = [&](floatx16 (&cur)[KB], const uint16_t *vb) __attribute__((always_inline)) {
-        lead(cur);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
