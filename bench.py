@@ -286,12 +286,17 @@ def ceilings(mfma_ms=10.0, launches=10):
            "hbm_read": []}
     wg = 512                                   # two 4-wave workgroups per CU
     res = torch.empty(wg * 256, dtype=torch.float32, device=dev)
-    flops_per_iter = wg * 4 * 4 * 32768.0
-    for dtype, data in (("fp16", "N(0,1)"), ("bf16", "N(0,1)"), ("fp16", "zeros")):
-        ops = synth.normal((wg * 256 * 16,), 9000, dtype, dev)
+    for dtype, data in (("fp16", "N(0,1)"), ("bf16", "N(0,1)"), ("fp16", "zeros"),
+                        ("fp8", "8 N(0,1) in E4M3")):
+        if dtype == "fp8":     # the FP8 leg's inputs: amp 8, i.e. 8 * N(0,1) rounded to E4M3
+            ops = synth.fp8_inputs(1, 1, wg * 256, 64, seed=9000, device=dev)[0]
+        else:
+            ops = synth.normal((wg * 256 * 16,), 9000, dtype, dev)
         if data == "zeros":
             ops.zero_()
-        code = 1 if dtype == "fp16" else 0
+        code = {"bf16": 0, "fp16": 1, "fp8": 2}[dtype]
+        flops_per_iter = wg * 4 * 4 * (131072.0 if dtype == "fp8" else 32768.0)
+        peak = PEAK_FP8_TFLOPS if dtype == "fp8" else PEAK_MFMA_TFLOPS
         probe = 2000
         ms, _ = timed(lambda: lib.fa_ceiling_mfma(ctypes.c_void_p(ops.data_ptr()),
                                                   ctypes.c_void_p(res.data_ptr()), wg, probe,
@@ -301,10 +306,12 @@ def ceilings(mfma_ms=10.0, launches=10):
                                                     ctypes.c_void_p(res.data_ptr()), wg, iters,
                                                     code, sp), launches)
         tf = flops_per_iter * iters / (ms * 1e-3) / 1e12
-        out["mfma"].append({"kernel": f"fa_ceiling_mfma_kernel<{dtype.upper()}>", "dtype": dtype,
+        kname = "fa_ceiling_mfma_fp8_kernel" if dtype == "fp8" else \
+            f"fa_ceiling_mfma_kernel<{dtype.upper()}>"
+        out["mfma"].append({"kernel": kname, "dtype": dtype,
                             "operands": data, "iters": iters, "avg_launch_ms": round(ms, 4),
                             "achieved": round(tf, 1), "unit": "TFLOP/s",
-                            "peak": PEAK_MFMA_TFLOPS, "frac": round(tf / PEAK_MFMA_TFLOPS, 4),
+                            "peak": peak, "frac": round(tf / peak, 4),
                             "clock_power": smi})
         print(f"ceiling mfma {dtype} {data}: {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
     nbytes = 4 << 30
@@ -806,8 +813,10 @@ def main():
                     help="timed fa_fwd_varlen calls for the varlen_fwd object (0: skip)")
     ap.add_argument("--paged-steps", type=int, default=50,
                     help="timed fa_decode_paged calls for the paged_decode object (0: skip)")
-    ap.add_argument("--only", choices=["fwd", "decode"], default=None,
-                    help="time one call only (for profiling runs)")
+    ap.add_argument("--only", choices=["fwd", "decode", "fp8", "bwd", "varlen", "paged"],
+                    default=None,
+                    help="run one kernel's leg only, with its --steps/--warmup or leg-step counts "
+                         "(for counter passes); prints that leg's object")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 3 times (the reference "
                          "kernel that scales the HBM byte counters)")
@@ -867,6 +876,15 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 3}))
+        return
+
+    legs = {"fp8": lambda: time_fp8(fa, synth, stream, args.fp8_steps,
+                                    max(FP8_MIN_WARMUP, args.warmup // 2)),
+            "bwd": lambda: time_bwd(fa, synth, stream, args.bwd_steps, BWD_WARMUP),
+            "varlen": lambda: time_varlen(fa, synth, stream, args.varlen_steps, VARLEN_WARMUP),
+            "paged": lambda: time_paged(fa, synth, stream, args.paged_steps, PAGED_WARMUP)}
+    if args.only in legs:
+        print(json.dumps({args.only: legs[args.only]()}), flush=True)
         return
 
     c = FWD
@@ -993,15 +1011,11 @@ def main():
                                    f"steps up to {args.sustain_s:g} s"),
         "device": torch.cuda.get_device_name(dev),
     }
-    if args.fp8_steps > 0 and args.only is None:
-        out["fp8_fwd"] = time_fp8(fa, synth, stream, args.fp8_steps,
-                                  max(FP8_MIN_WARMUP, args.warmup // 2))
-    if args.bwd_steps > 0 and args.only is None:
-        out["bwd"] = time_bwd(fa, synth, stream, args.bwd_steps, BWD_WARMUP)
-    if args.varlen_steps > 0 and args.only is None:
-        out["varlen_fwd"] = time_varlen(fa, synth, stream, args.varlen_steps, VARLEN_WARMUP)
-    if args.paged_steps > 0 and args.only is None:
-        out["paged_decode"] = time_paged(fa, synth, stream, args.paged_steps, PAGED_WARMUP)
+    for key, leg, n in (("fp8_fwd", "fp8", args.fp8_steps), ("bwd", "bwd", args.bwd_steps),
+                        ("varlen_fwd", "varlen", args.varlen_steps),
+                        ("paged_decode", "paged", args.paged_steps)):
+        if n > 0 and args.only is None:
+            out[key] = legs[leg]()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
