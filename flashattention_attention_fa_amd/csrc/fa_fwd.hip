@@ -498,20 +498,56 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     if ((ntiles - 1) & 1) last(sB, V1); else last(sA, V0);
 
     // Epilogue.  O^T accumulator: lane (li, lh), register r of block db holds
-    // dim 32*db + 8*(r/4) + 4*lh + r%4 of query my_q.
+    // dim 32*db + 8*(r/4) + 4*lh + r%4 of query my_q.  O is written through
+    // LDS (the K/V tile buffers are free once every wave is past the last
+    // tile), so that each store instruction writes whole rows: straight from
+    // the accumulator, one instruction would put 32 bytes into each of 32
+    // rows, and where rows lie far apart (the H*d stride of packed
+    // variable-length tensors) such partly written lines are evicted and
+    // written back more than once.
     const float l_tot = sum_halves(l_run);
-    if (my_q < N) {
-        const float inv = 1.f / l_tot;
-        float *orow = o + head + (size_t)my_q * RS + 4 * lh;
+    const float inv = 1.f / l_tot;
+    if (lse != nullptr && lh == 0 && my_q < N)
+        lse[lse_row0 + my_q] = (m_run + log2f(l_tot)) * kLn2;
+    // Each wave stages its 32 rows, DBP dim blocks (32*DBP dims) per pass,
+    // in its share of one tile buffer: row r holds CPR 16-byte chunks, chunk
+    // c stored at position c ^ (r % 16), which keeps the column writes and
+    // the row reads on distinct banks.
+    constexpr int WPB = C::WAVES / 4;                       // waves per tile buffer
+    constexpr int DBP = C::ELEMS * 2 / WPB / 4096;          // dim blocks per pass
+    constexpr int CPR = 8 * DBP;                            // chunks per staged row
+    constexpr int RPI = 64 / CPR;                           // rows per store instruction
+    static_assert(DBP >= 1 && DB % DBP == 0 && 64 % CPR == 0, "staging must fit a tile buffer");
+    uint16_t *const sbuf = (wave % 4) == 0 ? K0 : (wave % 4) == 1 ? K1 : (wave % 4) == 2 ? V0 : V1;
+    floatx4 *const stage = (floatx4 *)sbuf + (wave / 4) * 32 * CPR;
+    __syncthreads();
+    // The staging addresses depend on the lane only; taken from an opaque
+    // copy of it, the compiler cannot compute them before the loop (where
+    // they would stay live, and spill, across it).
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int eli = el & 31;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int pass = 0; pass < DB / DBP; ++pass) {
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-                *(floatx4 *)(orow + 32 * db + 8 * a) =
+        for (int dl = 0; dl < DBP; ++dl)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int db = pass * DBP + dl;
+                const int ch = 8 * dl + 2 * a + (el >> 5);
+                stage[eli * CPR + (ch ^ (eli % 16))] =
                     floatx4{oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv,
                             oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv};
-        if (lse != nullptr && lh == 0)
-            lse[lse_row0 + my_q] = (m_run + log2f(l_tot)) * kLn2;
+            }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int r = i * RPI + el / CPR, ch = el % CPR;
+            const floatx4 x = stage[r * CPR + (ch ^ (r % 16))];
+            if (qw + r < N)
+                *(floatx4 *)(o + head + (size_t)(qw + r) * RS + 32 * DBP * pass + 4 * ch) = x;
+        }
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
