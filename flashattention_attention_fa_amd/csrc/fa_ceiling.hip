@@ -35,6 +35,36 @@ __global__ __launch_bounds__(256, 2) void fa_ceiling_mfma_kernel(const u32x4 *__
     out[lane] = s;
 }
 
+// The same loop on the FP8 product of the FP8 forward,
+// v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 operands with neutral block
+// scales (twice the flops of the 16-bit product per instruction).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(256, 2) void fa_ceiling_mfma_fp8_kernel(const u32x4 *__restrict__ ops,
+                                                                    float *__restrict__ out,
+                                                                    int iters) {
+    const size_t lane = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const u32x4 a0 = ops[4 * lane], a1 = ops[4 * lane + 1], b0 = ops[4 * lane + 2],
+                b1 = ops[4 * lane + 3];
+    const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                     (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                     (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    floatx16 c0, c1, c2, c3;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c0[r] = c1[r] = c2[r] = c3[r] = 0.f;
+    for (int i = 0; i < iters; ++i) {
+        c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, 0, 0, 0, 127, 0, 127);
+        c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c1, 0, 0, 0, 127, 0, 127);
+        c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, a, c2, 0, 0, 0, 127, 0, 127);
+        c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, b, c3, 0, 0, 0, 127, 0, 127);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += (c0[r] + c1[r]) + (c2[r] + c3[r]);
+    out[lane] = s;
+}
+
 // Each workgroup streams one contiguous chunk of the buffer, as a decode
 // workgroup streams its shard of the cache: 256 lanes x 16 bytes per load,
 // four loads in flight per lane, through a buffer resource over the chunk
@@ -65,11 +95,14 @@ extern "C" {
 
 int fa_ceiling_mfma(const void *operands, float *out, int workgroups, int iters, int dtype,
                     hipStream_t stream) {
-    if (!operands || !out || workgroups < 1 || iters < 1 || (dtype != 0 && dtype != 1) ||
+    if (!operands || !out || workgroups < 1 || iters < 1 || dtype < 0 || dtype > 2 ||
         (reinterpret_cast<uintptr_t>(operands) & 15))
         return (int)hipErrorInvalidValue;
     const fa::u32x4 *ops = static_cast<const fa::u32x4 *>(operands);
-    if (dtype == 1)
+    if (dtype == 2)
+        hipLaunchKernelGGL(fa::fa_ceiling_mfma_fp8_kernel, dim3(workgroups), dim3(256), 0,
+                           stream, ops, out, iters);
+    else if (dtype == 1)
         hipLaunchKernelGGL(fa::fa_ceiling_mfma_kernel<fa::FP16>, dim3(workgroups), dim3(256), 0,
                            stream, ops, out, iters);
     else

@@ -29,12 +29,16 @@ extern "C" {
 
 /*
  * fa_ceiling_mfma -- `workgroups` workgroups of 4 waves; every wave issues
- * iters x 4 MFMAs v_mfma_f32_32x32x16_{bf16 (dtype 0), f16 (dtype 1)} in four
- * independent accumulation chains, i.e. 4 * 32768 * iters flops per wave.
- *   operands : workgroups * 256 lanes * 16 16-bit values (each lane's A and
- *              B operand), 16-byte aligned
+ * iters x 4 MFMAs in four independent accumulation chains:
+ *   dtype 0: v_mfma_f32_32x32x16_bf16, 4 * 32768 * iters flops per wave
+ *   dtype 1: v_mfma_f32_32x32x16_f16,  4 * 32768 * iters flops per wave
+ *   dtype 2: v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 (block scales 1),
+ *            4 * 131072 * iters flops per wave
+ *   operands : each lane's A and B operand, 32 bytes per lane (dtypes 0, 1)
+ *              or 64 bytes per lane (dtype 2), workgroups * 256 lanes,
+ *              16-byte aligned
  *   out      : workgroups * 256 floats (a checksum per lane, written)
- *   workgroups >= 1, iters >= 1, dtype 0 or 1
+ *   workgroups >= 1, iters >= 1
  */
 int fa_ceiling_mfma(const void *operands, float *out, int workgroups, int iters, int dtype,
                     hipStream_t stream);
