@@ -21,7 +21,7 @@ from pathlib import Path
 import torch
 
 __all__ = ["fwd", "fwd_varlen", "fwd_fp8", "bwd", "bwd_varlen", "bwd_workspace_bytes", "decode",
-           "decode_paged", "decode_workspace_bytes", "lib", "FAError", "LIB_PATH",
+           "decode_noalloc", "decode_paged", "decode_workspace_bytes", "lib", "FAError", "LIB_PATH",
            "HEADER_PATH", "status_string"]
 
 LIB_PATH = Path(__file__).resolve().parent / "libfa_amd.so"
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.fa_decode.restype = I
         L.fa_decode_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, I, P, S]
         L.fa_decode_ex.restype = I
+        L.fa_decode_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, I]
+        L.fa_decode_noalloc.restype = I
         L.fa_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, I, P, S]
         L.fa_decode_paged.restype = I
         L.fa_decode_workspace_bytes.argtypes = [I, I, I, I]
@@ -114,6 +116,9 @@ def _check_out(t, shape, device, what):
     _need(t.shape == tuple(shape) and t.dtype == torch.float32 and t.is_contiguous()
           and t.device == device, f"{what} must be a contiguous fp32 {list(shape)} tensor on {device}")
 
+
+# Bytes of fa_decode_noalloc's fixed per-device buffer (FA_DECODE_NOALLOC_MAX_BYTES).
+DECODE_NOALLOC_MAX_BYTES = 8 << 20
 
 
 def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
@@ -330,6 +335,24 @@ def decode(q, kcache, vcache, *, nsplit: int, out=None, lse=None, return_lse: bo
     st = lib().fa_decode_ex(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(out), _ptr(lse), B, Hq,
                             Hkv, L, d, int(nsplit), s, _DTYPE[q.dtype], _ptr(workspace), ws_bytes)
     _check(st, "fa_decode_ex")
+    return out, lse
+
+
+def decode_noalloc(q, kcache, vcache, *, nsplit: int, out, lse=None, stream=None):
+    """Split-KV flash-decode through fa_decode_noalloc: the library allocates
+    nothing (its shard partials live in a fixed per-device buffer of
+    DECODE_NOALLOC_MAX_BYTES), and this binding allocates nothing either, so
+    the caller passes ``out`` [B, Hq, d] fp32 (and optionally ``lse`` [B, Hq]
+    fp32).  Calls that overlap in time on one GPU share that buffer and race.
+    Returns (out, lse)."""
+    B, Hq, Hkv, L, d = _decode_args(q, kcache, vcache)
+    _check_out(out, (B, Hq, d), q.device, "out")
+    if lse is not None:
+        _check_out(lse, (B, Hq), q.device, "lse")
+    st = lib().fa_decode_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(out), _ptr(lse), B,
+                                 Hq, Hkv, L, d, int(nsplit), _stream(stream, q.device),
+                                 _DTYPE[q.dtype])
+    _check(st, "fa_decode_noalloc")
     return out, lse
 
 

@@ -18,6 +18,9 @@ namespace {
 // Per-head byte offsets are 32-bit (buffer addressing): seq_len * 128 * 2 < 2^32.
 constexpr int kMaxSeq = 1 << 23;
 
+static_assert(FA_DECODE_NOALLOC_MAX_BYTES == fa::kDecodeScratchBytes,
+              "the header's no-alloc limit must match the device buffer");
+
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -369,6 +372,29 @@ fa_status_t fa_decode_paged(const void *q, const void *kpages, const void *vpage
         a.pages_per_seq = pages_per_seq;
         a.num_pages = num_pages;
         return fa::launch_decode(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    } catch (...) {
+        return FA_ERR_INTERNAL;
+    }
+}
+
+fa_status_t fa_decode_noalloc(const void *q, const void *kcache, const void *vcache, float *o,
+                              float *lse, int B, int Hq, int Hkv, int L, int d, int nsplit,
+                              hipStream_t stream, fa_dtype_t dtype) {
+    try {
+        if (B == 0 || Hq == 0) {
+            if (B < 0 || Hq < 0 || Hkv < 1 || L < 1 || nsplit < 1) return FA_ERR_SHAPE;
+            return FA_OK;
+        }
+        fa_status_t st = check_decode(q, kcache, vcache, o, lse, B, Hq, Hkv, L, d, nsplit, dtype);
+        if (st != FA_OK) return st;
+        const int ns = nsplit > L ? L : nsplit;
+        const size_t need = fa_decode_workspace_bytes(B, Hq, d, ns);
+        if (need == 0) return FA_ERR_SHAPE;
+        if (need > fa::kDecodeScratchBytes) return FA_ERR_WORKSPACE;
+        void *ws = nullptr;
+        if (fa::decode_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+        return run_decode(q, kcache, vcache, o, lse, B, Hq, Hkv, L, d, ns, stream, dtype, ws,
+                          fa::kDecodeScratchBytes);
     } catch (...) {
         return FA_ERR_INTERNAL;
     }

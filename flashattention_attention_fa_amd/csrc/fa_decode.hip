@@ -26,6 +26,9 @@
 //   like V, see load()); two S^T blocks (32 keys) form the P^T
 //   operand of O^T (16 dims x 16 heads) += V^T (16 dims x 32 keys) P^T, with
 //   V^T read from a row-major LDS copy of the V rows by transposing reads.
+#include <mutex>
+#include <vector>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -463,5 +466,36 @@ static hipError_t launch_dtype(const DecodeArgs &a, hipStream_t s) {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     return a.dtype == 1 ? launch_dtype<FP16x16>(a, stream) : launch_dtype<BF16x16>(a, stream);
 }
+
+// Fixed partial-result buffer for callers that cannot allocate: every GPU the
+// library runs on holds one copy from the module load until the process
+// ends.  In host code `scratch` names a host-side stand-in, not the device
+// copy, so the kernels get the device address that hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+std::mutex g_scratch_mutex;
+std::vector<void *> g_scratch;   // device address of `scratch`, by HIP device id
+}  // namespace
+
+hipError_t decode_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if ((size_t)dev >= g_scratch.size()) g_scratch.resize((size_t)dev + 1, nullptr);
+    if (g_scratch[(size_t)dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch[(size_t)dev] = p;
+    }
+    *ptr = g_scratch[(size_t)dev];
+    return hipSuccess;
+}
+
 
 }  // namespace fa

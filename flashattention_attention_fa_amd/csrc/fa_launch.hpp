@@ -72,4 +72,12 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
+// The decode partials of fa_decode_noalloc live in a fixed device array of
+// this many bytes (one per GPU, for the life of the process).
+constexpr size_t kDecodeScratchBytes = size_t(8) << 20;
+
+// Device address of that array on the current device (looked up once per
+// device; no allocation).
+hipError_t decode_scratch(void **ptr);
+
 }  // namespace fa

@@ -42,6 +42,9 @@ typedef enum {
  * with fp32 accumulation; outputs are always fp32. */
 typedef enum { FA_BF16 = 0, FA_FP16 = 1 } fa_dtype_t;
 
+/* Size of fa_decode_noalloc's fixed per-device buffer, in bytes. */
+#define FA_DECODE_NOALLOC_MAX_BYTES ((size_t)8 << 20)
+
 /*
  * fa_fwd -- exact softmax attention, computed tile by tile without storing
  * the N x N score matrix (dailyaiworld page, introduction: FlashAttention's
@@ -215,6 +218,26 @@ fa_status_t fa_decode_ex(const void *q, const void *kcache,
                          int Hq, int Hkv, int L, int d, int nsplit,
                          hipStream_t stream, fa_dtype_t dtype,
                          void *workspace, size_t workspace_bytes);
+
+/*
+ * fa_decode_noalloc -- fa_decode_ex for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops or harnesses that
+ * forbid hipMalloc): same arguments minus the workspace, same results, and
+ * no allocation of any kind.  The shard partials go to a fixed buffer of
+ * FA_DECODE_NOALLOC_MAX_BYTES (8 MiB) that the library keeps in device memory
+ * on every GPU it runs on, from the module load until the process ends; its
+ * address is looked up (not allocated) on the first call on each device.
+ * A call needing fa_decode_workspace_bytes(B, Hq, d, min(nsplit, L)) bytes
+ * more than that returns FA_ERR_WORKSPACE before any HIP call (at d = 128:
+ * about B * Hq * min(nsplit, L) <= 16000).  Every call on
+ * one GPU shares that buffer: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and give wrong results.
+ *   lse : [B, Hq] fp32, device, or NULL
+ */
+fa_status_t fa_decode_noalloc(const void *q, const void *kcache,
+                              const void *vcache, float *o, float *lse, int B,
+                              int Hq, int Hkv, int L, int d, int nsplit,
+                              hipStream_t stream, fa_dtype_t dtype);
 
 /*
  * fa_decode_paged -- fa_decode_ex over a paged key/value cache with a length

@@ -21,6 +21,7 @@ def test_exports_every_declared_function(L):
     names = fa.declared_functions()
     assert set(names) >= {"fa_fwd", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd", "fa_bwd_varlen",
                           "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_ex", "fa_decode_paged",
+                          "fa_decode_noalloc",
                           "fa_decode_workspace_bytes",
                           "fa_status_string", "fa_version"}
     for n in names:
@@ -231,6 +232,35 @@ def test_decode_ex_workspace(L):
     # nsplit larger than L is clamped to L before sizing the workspace
     assert L.fa_decode_workspace_bytes(1, 4, 128, 100) < L.fa_decode_workspace_bytes(1, 4, 128, 200)
     assert dec_ex(L, Lk=3, nsplit=50, ws_bytes=L.fa_decode_workspace_bytes(1, 4, 128, 3) - 1) == WS
+
+
+def dec_noalloc(L, lse=None, **kw):
+    a = dict(q=A, k=A, v=A, o=A, B=1, Hq=4, Hkv=2, Lk=100, d=128, nsplit=4, dtype=0)
+    a.update(kw)
+    return L.fa_decode_noalloc(a["q"], a["k"], a["v"], a["o"], lse, a["B"], a["Hq"], a["Hkv"],
+                               a["Lk"], a["d"], a["nsplit"], None, a["dtype"])
+
+
+def test_decode_noalloc_validation(L):
+    """Every rejection happens before the library looks up its device buffer
+    (no HIP call), including a call whose partials would not fit in it."""
+    assert fa.DECODE_NOALLOC_MAX_BYTES == 8 << 20
+    assert dec_noalloc(L, q=None) == NULL
+    assert dec_noalloc(L, o=None) == NULL
+    assert dec_noalloc(L, Hq=6, Hkv=4) == SHAPE
+    assert dec_noalloc(L, Lk=0) == SHAPE
+    assert dec_noalloc(L, nsplit=0) == SHAPE
+    assert dec_noalloc(L, d=96) == UNSUP
+    assert dec_noalloc(L, dtype=2) == UNSUP
+    assert dec_noalloc(L, v=MIS) == ALIGN
+    assert dec_noalloc(L, lse=A + 2) == ALIGN
+    assert dec_noalloc(L, q=None, B=0) == OK
+    # partials of B*Hq*nsplit rows x (d + 1) floats must fit in 8 MiB
+    fits = L.fa_decode_workspace_bytes(8, 32, 128, 16)
+    assert fits <= fa.DECODE_NOALLOC_MAX_BYTES
+    big = L.fa_decode_workspace_bytes(8, 32, 128, 64)
+    assert big > fa.DECODE_NOALLOC_MAX_BYTES
+    assert dec_noalloc(L, B=8, Hq=32, Hkv=8, Lk=32768, nsplit=64) == WS
 
 
 def test_python_binding_rejects_bad_tensors():

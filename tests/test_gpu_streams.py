@@ -157,6 +157,8 @@ def test_binding_rejects_bad_output_buffers():
         fa.decode(qd, kc, vc, nsplit=2, lse=torch.empty(2, 3, device=DEV))
     with pytest.raises(ValueError):
         fa.decode(qd, kc, vc, nsplit=2, out=torch.empty(2, 4, 64))
+    with pytest.raises(ValueError):
+        fa.decode_noalloc(qd, kc, vc, nsplit=2, out=torch.empty(2, 4, 32, device=DEV))
     kp = synth.normal((4, 16, 2, 64), 4602, "bf16", DEV)
     table = torch.zeros(2, 2, dtype=torch.int32, device=DEV)
     seq = torch.full((2,), 20, dtype=torch.int32, device=DEV)
