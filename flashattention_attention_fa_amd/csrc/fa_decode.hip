@@ -27,6 +27,7 @@
 //   operand of O^T (16 dims x 16 heads) += V^T (16 dims x 32 keys) P^T, with
 //   V^T read from a row-major LDS copy of the V rows by transposing reads.
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "fa_device.hpp"
@@ -86,8 +87,13 @@ struct PagedCache {
     int page_size, pages_per_seq, num_pages;
 };
 
-template <typename T, int D, bool PAGED>
-__global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
+// Paged caches store the rows of all Hkv heads of a token next to each
+// other, so one head's rows are Hkv*D*2 bytes apart.  A paged workgroup
+// takes HG adjacent kv heads of the shard with WH waves each: its waves then
+// read HG*D*2 contiguous bytes of every token row instead of one head's
+// D*2 bytes, which DRAM serves far better.  8 waves fill a CU.
+template <typename T, int D, bool PAGED, int HG, int WH>
+__global__ __launch_bounds__(64 * HG * WH, 8 / (HG * WH)) void fa_decode_split_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, float *__restrict__ ws_o,
     float *__restrict__ ws_lse, int Hq, int Hkv, int L, int nsplit, int chunk,
@@ -97,20 +103,26 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
     typedef typename T::scalar scalar;
     constexpr int LD = C::LD;
 
+    static_assert((HG == 1 && WH == C::WAVES) || PAGED, "head groups are for paged caches");
+    constexpr int NW = WH * HG;           // waves of the workgroup
+    constexpr int NT = 64 * NW;
+
     // V tile staging, one slab per wave; reused for the final merge.
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[C::WAVES][C::V_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[NW][C::V_ELEMS];
     // Paged: the K rows of the step, same layout as the V slab.
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[PAGED ? C::WAVES : 1][PAGED ? C::V_ELEMS : 1];
-    __shared__ float sm_m[C::WAVES][C::COLS], sm_l[C::WAVES][C::COLS];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[PAGED ? NW : 1][PAGED ? C::V_ELEMS : 1];
+    __shared__ float sm_m[NW][C::COLS], sm_l[NW][C::COLS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar block-table reads
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar block-table reads
+    const int hh = wave_id / WH;   // kv head of the group
+    const int wave = wave_id % WH;   // wave among the head's WH
     const int lj = lane & 15;   // column (query head) / A-operand row
     const int lg = lane >> 4;   // contraction group 0..3
 
     const int s = blockIdx.x;
-    const int g = blockIdx.y / ncc, cc = blockIdx.y % ncc;
+    const int g = (blockIdx.y / ncc) * HG + hh, cc = blockIdx.y % ncc;
     const int b = blockIdx.z;
     const int G = Hq / Hkv;
     const int hq0 = g * G + cc * C::COLS;
@@ -191,8 +203,8 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
-    uint16_t *vt = Vs[wave];
-    uint16_t *kt = Ks[PAGED ? wave : 0];
+    uint16_t *vt = Vs[wave_id];
+    uint16_t *kt = Ks[PAGED ? wave_id : 0];
     // ds_read_b64_tr_b16 addressing: lane j of group lg points at row
     // 4*lg + j/4, column 4*(j%4) (plus the 16-dim block offset).
     const uint16_t *va = vt + (4 * lg + (lj >> 2)) * LD + 4 * (lj & 3);
@@ -280,52 +292,54 @@ __global__ __launch_bounds__(256, 2) void fa_decode_split_kernel(
         DecBuf<D, PAGED> A, B;
         int n = wave;
         if (n < nblk) load(A, n);
-        for (; n < nblk; n += 2 * C::WAVES) {
-            if (n + C::WAVES < nblk) load(B, n + C::WAVES);
+        for (; n < nblk; n += 2 * WH) {
+            if (n + WH < nblk) load(B, n + WH);
             compute(A, n);
-            if (n + C::WAVES >= nblk) break;
-            if (n + 2 * C::WAVES < nblk) load(A, n + 2 * C::WAVES);
-            compute(B, n + C::WAVES);
+            if (n + WH >= nblk) break;
+            if (n + 2 * WH < nblk) load(A, n + 2 * WH);
+            compute(B, n + WH);
         }
     }
 
-    // Merge the 4 wave states.  Per column: M = max_w m_w,
+    // Merge the WH wave states of each head.  Per column: M = max_w m_w,
     // Lsum = sum_w l_w 2^(m_w - M), O = sum_w 2^(m_w - M) O_w / Lsum.
     float l_w = l_run + __shfl_xor(l_run, 16, 64);
     l_w += __shfl_xor(l_w, 32, 64);
     if (lg == 0) {
-        sm_m[wave][lj] = m_run;
-        sm_l[wave][lj] = l_w;
+        sm_m[wave_id][lj] = m_run;
+        sm_l[wave_id][lj] = l_w;
     }
     __syncthreads();
+    const int w0 = hh * WH;   // first wave of this head
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < C::WAVES; ++w) M = fmaxf(M, sm_m[w][lj]);
+    for (int w = 0; w < WH; ++w) M = fmaxf(M, sm_m[w0 + w][lj]);
     const float Mb = M == -INFINITY ? 0.f : M;
     float Lsum = 0.f;
 #pragma unroll
-    for (int w = 0; w < C::WAVES; ++w)
-        Lsum += sm_l[w][lj] * __builtin_amdgcn_exp2f(sm_m[w][lj] - Mb);
+    for (int w = 0; w < WH; ++w)
+        Lsum += sm_l[w0 + w][lj] * __builtin_amdgcn_exp2f(sm_m[w0 + w][lj] - Mb);
     const float f = Lsum > 0.f ? __builtin_amdgcn_exp2f(m_run - Mb) / Lsum : 0.f;
-    // Scaled wave outputs go to LDS as part[w][col][d] (reusing the V slabs).
-    // O^T accumulator: lane (lj, lg), register r of block db holds dim
-    // 16db + 4lg + r of head hq0 + lj.
+    // Scaled wave outputs go to LDS as part[wave][col][d] (reusing the V
+    // slabs).  O^T accumulator: lane (lj, lg), register r of block db holds
+    // dim 16db + 4lg + r of head hq0 + lj.
     float *part = reinterpret_cast<float *>(&Vs[0][0]);
-    static_assert(C::WAVES * C::COLS * D * 4 <= (int)sizeof(Vs), "merge buffer");
+    static_assert(NW * C::COLS * D * 4 <= (int)sizeof(Vs), "merge buffer");
     __syncthreads();
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
-        *(floatx4 *)&part[(wave * C::COLS + lj) * D + 16 * db + 4 * lg] = oacc[db] * f;
+        *(floatx4 *)&part[(wave_id * C::COLS + lj) * D + 16 * db + 4 * lg] = oacc[db] * f;
     __syncthreads();
-    for (int idx = tid; idx < ncol * D; idx += C::THREADS) {
-        const int col = idx / D, d = idx % D;
+    // Head x of the group writes query heads hq0 - hh*G + x*G + col.
+    for (int idx = tid; idx < HG * ncol * D; idx += NT) {
+        const int x = idx / (ncol * D), col = (idx / D) % ncol, d = idx % D;
         float acc = 0.f;
 #pragma unroll
-        for (int w = 0; w < C::WAVES; ++w) acc += part[(w * C::COLS + col) * D + d];
-        ws_o[(((size_t)b * Hq + hq0 + col) * nsplit + s) * D + d] = acc;
+        for (int w = 0; w < WH; ++w) acc += part[((x * WH + w) * C::COLS + col) * D + d];
+        ws_o[(((size_t)b * Hq + hq0 + (x - hh) * G + col) * nsplit + s) * D + d] = acc;
     }
-    if (tid < ncol)
-        ws_lse[((size_t)b * Hq + hq0 + tid) * nsplit + s] =
+    if (wave == 0 && lane < ncol)
+        ws_lse[((size_t)b * Hq + hq0 + lane) * nsplit + s] =
             Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
@@ -424,6 +438,10 @@ __global__ __launch_bounds__(128) void fa_decode_combine_kernel(
     if (lse != nullptr && tid == 0) lse[row] = total;
 }
 
+// Workgroups a paged launch keeps at least (one per CU of MI355X), when it
+// chooses how many kv heads one workgroup takes.
+constexpr long long kDecodeMinWorkgroups = 256;
+
 template <typename T, int D>
 static hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
     typedef DecTile<D> C;
@@ -432,16 +450,27 @@ static hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
     const float c = kLog2e / sqrtf((float)D);
     if ((long long)a.Hkv * ncc > 65535 || a.B > 65535) return hipErrorInvalidConfiguration;
     PagedCache pc = {a.block_table, a.seq_lens, a.page_size, a.pages_per_seq, a.num_pages};
-    if (a.block_table != nullptr)
-        hipLaunchKernelGGL((fa_decode_split_kernel<T, D, true>), dim3(a.nsplit, a.Hkv * ncc, a.B),
-                           dim3(C::THREADS), 0, stream, (const uint16_t *)a.q,
-                           (const uint16_t *)a.k, (const uint16_t *)a.v, a.ws_o, a.ws_lse,
-                           a.Hq, a.Hkv, a.L, a.nsplit, a.chunk, ncc, c, pc);
+    auto split = [&](auto paged, auto hg, auto wh) {
+        constexpr int HG = decltype(hg)::value, WH = decltype(wh)::value;
+        hipLaunchKernelGGL((fa_decode_split_kernel<T, D, decltype(paged)::value, HG, WH>),
+                           dim3(a.nsplit, a.Hkv / HG * ncc, a.B), dim3(64 * HG * WH), 0, stream,
+                           (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
+                           a.ws_o, a.ws_lse, a.Hq, a.Hkv, a.L, a.nsplit, a.chunk, ncc, c, pc);
+    };
+    typedef std::integral_constant<int, 1> I1;
+    typedef std::integral_constant<int, 2> I2;
+    typedef std::integral_constant<int, 4> I4;
+    // Paged: the largest head group that divides Hkv and still gives every
+    // CU a workgroup.
+    const long long units = (long long)a.nsplit * a.B * ncc;
+    if (a.block_table == nullptr)
+        split(std::false_type{}, I1{}, I4{});
+    else if (a.Hkv % 4 == 0 && units * (a.Hkv / 4) >= kDecodeMinWorkgroups)
+        split(std::true_type{}, I4{}, I2{});
+    else if (a.Hkv % 2 == 0)
+        split(std::true_type{}, I2{}, I4{});
     else
-        hipLaunchKernelGGL((fa_decode_split_kernel<T, D, false>), dim3(a.nsplit, a.Hkv * ncc, a.B),
-                           dim3(C::THREADS), 0, stream, (const uint16_t *)a.q,
-                           (const uint16_t *)a.k, (const uint16_t *)a.v, a.ws_o, a.ws_lse,
-                           a.Hq, a.Hkv, a.L, a.nsplit, a.chunk, ncc, c, pc);
+        split(std::true_type{}, I1{}, I4{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.nsplit <= 16)
@@ -496,6 +525,5 @@ hipError_t decode_scratch(void **ptr) {
     *ptr = g_scratch[(size_t)dev];
     return hipSuccess;
 }
-
 
 }  // namespace fa

@@ -90,6 +90,14 @@ def test_dtypes_dims_groups(orc):
     run(orc, [512, 513], 20, 1, 128, 128, nsplit=6, dtype="fp16", seed=203)
 
 
+def test_four_head_groups(orc):
+    """Shapes whose launch gives each workgroup four kv heads (two waves
+    each): Hkv a multiple of 4 and at least 256 such workgroups.  Ragged
+    lengths, an empty sequence, shards past a sequence's end."""
+    run(orc, [1, 33, 500, 0, 1200, 64, 2049, 7], 16, 8, 128, 16, nsplit=40, seed=300)
+    run(orc, [100, 3000, 1, 257], 16, 4, 64, 32, nsplit=64, dtype="fp16", seed=301)
+
+
 def test_matches_dense_layout():
     """A paged cache holding the same keys as a dense one, one length for
     all sequences and shard boundaries on 32-key blocks: identical results."""
