@@ -203,7 +203,7 @@ def trace_summary(paths, warmup, steps, fp8_steps, bwd_steps, varlen_steps, page
     # (leg, demangled name prefix, launches skipped, launches timed, algorithmic work, peak)
     legs = [("fwd", "fa::fa_fwd_kernel<fa::FP16, 128, false, false>(", warmup, steps,
              ("TFLOP/s", flops, PEAK_MFMA_TFLOPS)),
-            ("decode", "fa::fa_decode_split_kernel<fa::BF16x16, 128, false>(", warmup, steps,
+            ("decode", "fa::fa_decode_split_kernel<fa::BF16x16, 128, false, 1, 4>(", warmup, steps,
              ("GB/s", decode_bytes(DEC["B"], DEC["Hq"], DEC["Hkv"], DEC["L"], DEC["d"]),
               PEAK_HBM_GBS)),
             ("decode", "fa::fa_decode_combine_few_kernel<16>(", warmup, steps, None),
@@ -215,7 +215,7 @@ def trace_summary(paths, warmup, steps, fp8_steps, bwd_steps, varlen_steps, page
              None),
             ("varlen_fwd", "fa::fa_fwd_kernel<fa::FP16, 128, false, true>(", VARLEN_WARMUP,
              varlen_steps, None),
-            ("paged_decode", "fa::fa_decode_split_kernel<fa::BF16x16, 128, true>(", PAGED_WARMUP,
+            ("paged_decode", "fa::fa_decode_split_kernel<fa::BF16x16, 128, true, 4, 2>(", PAGED_WARMUP,
              paged_steps, ("GB/s", decode_bytes(DEC["B"], DEC["Hq"], DEC["Hkv"], DEC["L"],
                                                   DEC["d"]), PEAK_HBM_GBS))]
     out = []
@@ -332,6 +332,104 @@ def ceilings(mfma_ms=10.0, launches=10):
                                     "frac": round(gbs / PEAK_HBM_GBS, 4), "clock_power": smi})
             print(f"ceiling read wg={wgs} nt={nt}: {gbs:.1f} GB/s", file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
+
+
+# Kernels whose HBM traffic profiles/traffic.json records: key, demangled
+# name prefix, and the sources whose digest the record carries.
+TRAFFIC_KERNELS = {
+    "fa_fwd_kernel": ("fa::fa_fwd_kernel<fa::FP16, 128, false, false>(", ("fa_fwd.hip", "fa_device.hpp")),
+    "fa_fwd_fp8_kernel": ("fa::fa_fwd_fp8_kernel<128, false>(", ("fa_fwd_fp8.hip", "fa_device.hpp")),
+    "fa_bwd_dq_kernel": ("fa::fa_bwd_dq_kernel<fa::FP16, 128, false, false>(", ("fa_bwd.hip", "fa_device.hpp")),
+    "fa_bwd_dkdv_kernel": ("fa::fa_bwd_dkdv_kernel<fa::FP16, 128, false, false>(", ("fa_bwd.hip", "fa_device.hpp")),
+    "fa_decode_split_kernel": ("fa::fa_decode_split_kernel<fa::BF16x16, 128, false, 1, 4>(",
+                               ("fa_decode.hip", "fa_device.hpp")),
+    "fa_fwd_varlen_kernel": ("fa::fa_fwd_kernel<fa::FP16, 128, false, true>(", ("fa_fwd.hip", "fa_device.hpp")),
+    "fa_decode_paged_split_kernel": ("fa::fa_decode_split_kernel<fa::BF16x16, 128, true, 4, 2>(",
+                                     ("fa_decode.hip", "fa_device.hpp")),
+}
+
+
+def counter_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path=None):
+    """HBM bytes per launch of each kernel of TRAFFIC_KERNELS from rocprofv3
+    --pmc FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch, summed over the
+    counter's instances), each scaled by what the same counter reads for the
+    --calibrate-copy run's 1 GiB device copy.  Prints one JSON line per
+    kernel; with out_path, also writes them as the traffic record bench.py
+    reads (keyed by kernel, with the digest of its sources)."""
+    import csv
+    import glob
+    import statistics as st
+    csv.field_size_limit(1 << 30)
+
+    def per_dispatch(d):
+        tot = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    key = (r["Kernel_Name"], r["Dispatch_Id"])
+                    tot[key] = tot.get(key, 0.0) + float(r["Counter_Value"])
+        return tot
+
+    def copy_kib(d):
+        # the device copy is the only dispatch reading or writing a full GiB
+        return max(per_dispatch(d).values())
+
+    scale_f = (1 << 20) / copy_kib(copy_fetch_dir)     # bytes of the copy / KiB read
+    scale_w = (1 << 20) / copy_kib(copy_write_dir)
+    fetch, write = per_dispatch(fetch_dir), per_dispatch(write_dir)
+    record = {}
+    for key, (prefix, sources) in TRAFFIC_KERNELS.items():
+        match = lambda name: name.startswith(prefix) or name.startswith("void " + prefix)
+        fk = [v for (n, _), v in fetch.items() if match(n)]
+        wk = [v for (n, _), v in write.items() if match(n)]
+        if not fk or not wk:
+            continue
+        fb = st.median(fk) * 1024 * scale_f
+        wb = st.median(wk) * 1024 * scale_w
+        record[key] = {"kernel": prefix[:-1], "source_digest": source_digest(*sources),
+                       "hbm_bytes_per_launch": int(round(fb + wb)),
+                       "fetch_bytes_per_launch": int(round(fb)),
+                       "write_bytes_per_launch": int(round(wb)),
+                       "fetch_kib_raw_median": st.median(fk), "write_kib_raw_median": st.median(wk),
+                       "dispatches": [len(fk), len(wk)],
+                       "fetch_scale": scale_f, "write_scale": scale_w}
+        print(json.dumps(dict(record[key], name=key)))
+    if out_path:
+        with open(out_path, "w") as f:
+            json.dump(record, f, indent=1)
+            f.write("\n")
+
+
+def counter_table(dirs):
+    """Median per dispatch of every counter that rocprofv3 --pmc runs of this
+    script recorded (output directories `dirs`), for each kernel of
+    TRAFFIC_KERNELS; one JSON line per kernel."""
+    import csv
+    import glob
+    import statistics as st
+    csv.field_size_limit(1 << 30)
+    vals, dur = {}, {}
+    for n, d in enumerate(dirs):
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    key = (r["Kernel_Name"], r["Dispatch_Id"], r["Counter_Name"])
+                    vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+                    dur[(r["Kernel_Name"], n, r["Dispatch_Id"])] = \
+                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    for name, (prefix, _) in TRAFFIC_KERNELS.items():
+        match = lambda k: k.startswith(prefix) or k.startswith("void " + prefix)
+        per = {}
+        for (kname, _, ctr), v in vals.items():
+            if match(kname):
+                per.setdefault(ctr, []).append(v)
+        times = [t for (kname, _, _), t in dur.items() if match(kname)]
+        if times:
+            per["time_us"] = times
+        if per:
+            print(json.dumps({"name": name, "kernel": prefix[:-1],
+                              "dispatches": max(len(v) for c, v in per.items() if c != "time_us"),
+                              **{c: st.median(v) for c, v in sorted(per.items())}}))
 
 
 def cpu_baseline(seconds_target=15.0):
@@ -834,6 +932,16 @@ def main():
                     help="instead of running: per-kernel times over the timed launches only, from "
                          "rocprofv3 kernel-trace CSVs of a run of this script with the same "
                          "--steps/--warmup/leg-step options (one JSON line per kernel)")
+    ap.add_argument("--counter-summary", nargs=4, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="instead of running: HBM bytes per launch per kernel from rocprofv3 "
+                         "--pmc FETCH_SIZE / WRITE_SIZE output directories of this script and of "
+                         "its --calibrate-copy run")
+    ap.add_argument("--counter-table", nargs="+", default=None, metavar="DIR",
+                    help="instead of running: median per dispatch of every counter of rocprofv3 "
+                         "--pmc output directories, per kernel")
+    ap.add_argument("--write-traffic", default=None, metavar="JSON",
+                    help="with --counter-summary: also write the per-kernel record to JSON")
     ap.add_argument("--sustain-s", type=float, default=3.0,
                     help="keep running the step (untimed) until this many seconds after the "
                          "timed steps began, so the clock/power readings cover several refreshes")
@@ -841,6 +949,12 @@ def main():
                     help="instead of the step: the achievable MFMA and HBM-read ceilings "
                          "(libfa_ceiling.so), with clock and power")
     args = ap.parse_args()
+    if args.counter_table:
+        counter_table(args.counter_table)
+        return
+    if args.counter_summary:
+        counter_summary(*args.counter_summary, out_path=args.write_traffic)
+        return
     if args.trace_summary:
         for rec in trace_summary(args.trace_summary, args.warmup, args.steps, args.fp8_steps,
                                  args.bwd_steps, args.varlen_steps, args.paged_steps):

@@ -45,3 +45,57 @@ def test_trace_summary_counts_only_timed_launches(tmp_path):
     assert len(rec) == 1 and rec[0]["leg"] == "fwd"
     assert rec[0]["timed"] == 3 and rec[0]["skipped"] == 2 and rec[0]["launches_in_trace"] == 6
     assert rec[0]["avg_us"] == 2000.0 and rec[0]["median_us"] == 2000.0
+
+
+def _counter_csv(d, rows):
+    """rocprofv3 --pmc output layout: one counter_collection.csv under d."""
+    d.mkdir(parents=True)
+    lines = ['"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"']
+    for disp, name, ctr, val, t0, t1 in rows:
+        lines.append(f'"{disp}","{name}","{ctr}","{val}","{t0}","{t1}"')
+    (d / "run_counter_collection.csv").write_text("\n".join(lines) + "\n")
+
+
+def test_counter_summary_scales_by_the_copy(tmp_path):
+    """--counter-summary sums a counter over its instances per dispatch, takes
+    the median over dispatches and scales KiB by what the same counter read
+    for the 1 GiB calibration copy (synthetic counter files, no GPU)."""
+    import json
+    fwd = "void fa::fa_fwd_kernel<fa::FP16, 128, false, false>(x)"
+    copy = "copy_kernel"
+    # fetch: 2 instances per dispatch; dispatch sums 300, 500, 400 KiB -> median 400
+    _counter_csv(tmp_path / "f", [(1, fwd, "FETCH_SIZE", 100, 0, 1), (1, fwd, "FETCH_SIZE", 200, 0, 1),
+                                  (2, fwd, "FETCH_SIZE", 250, 0, 1), (2, fwd, "FETCH_SIZE", 250, 0, 1),
+                                  (3, fwd, "FETCH_SIZE", 400, 0, 1)])
+    _counter_csv(tmp_path / "w", [(1, fwd, "WRITE_SIZE", 64, 0, 1), (2, fwd, "WRITE_SIZE", 64, 0, 1)])
+    # the copy's fetch counter reads half the bytes it moves (factor 2), write reads all (factor 1)
+    _counter_csv(tmp_path / "cf", [(1, copy, "FETCH_SIZE", 1 << 19, 0, 1), (2, "small", "FETCH_SIZE", 5, 0, 1)])
+    _counter_csv(tmp_path / "cw", [(1, copy, "WRITE_SIZE", 1 << 20, 0, 1)])
+    out = tmp_path / "traffic.json"
+    r = run("--counter-summary", str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"),
+            str(tmp_path / "cw"), "--write-traffic", str(out))
+    assert r.returncode == 0, r.stderr
+    rec = [json.loads(x) for x in r.stdout.splitlines()]
+    assert [x["name"] for x in rec] == ["fa_fwd_kernel"]
+    assert rec[0]["fetch_bytes_per_launch"] == 400 * 1024 * 2
+    assert rec[0]["write_bytes_per_launch"] == 64 * 1024
+    assert rec[0]["dispatches"] == [3, 2]
+    assert json.loads(out.read_text())["fa_fwd_kernel"]["hbm_bytes_per_launch"] == (800 + 64) * 1024
+
+
+def test_counter_table_medians_per_dispatch(tmp_path):
+    """--counter-table reports each counter's median per dispatch and the
+    median duration of its dispatches over all passes (synthetic files)."""
+    import json
+    dq = "void fa::fa_bwd_dq_kernel<fa::FP16, 128, false, false>(x)"
+    _counter_csv(tmp_path / "a", [(1, dq, "SQ_INSTS_MFMA", 10, 0, 2000), (2, dq, "SQ_INSTS_MFMA", 30, 0, 4000),
+                                  (3, dq, "SQ_INSTS_MFMA", 20, 0, 3000)])
+    _counter_csv(tmp_path / "b", [(1, dq, "SQ_WAVES", 7, 0, 1000), (1, dq, "SQ_WAVES", 1, 0, 1000)])
+    r = run("--counter-table", str(tmp_path / "a"), str(tmp_path / "b"))
+    assert r.returncode == 0, r.stderr
+    rec = [json.loads(x) for x in r.stdout.splitlines()]
+    assert len(rec) == 1 and rec[0]["name"] == "fa_bwd_dq_kernel"
+    assert rec[0]["SQ_INSTS_MFMA"] == 20 and rec[0]["SQ_WAVES"] == 8
+    assert rec[0]["dispatches"] == 3
+    # durations of every dispatch of both passes: 2, 4, 3 and 1 us
+    assert rec[0]["time_us"] == 2.5
