@@ -34,14 +34,13 @@
 //                 (then m, O and l are updated as above and the tile's
 //                 weights recomputed).  Any m that keeps the weights finite
 //                 gives the same O and lse; the bound keeps them small.
-//                 With bf16 weights the bound is tighter: a tile whose
-//                 weights would more than double a lane's running sum asks
-//                 too, so that a weight which dominates its row is exactly 1
-//                 (see kTileShareBf16).
 //   O^T += V^T P^T  P^T is the S^T accumulator converted to 16 bits in
 //                 place; V^T comes from the row-major V tile through the
 //                 transposing LDS read.
-// Epilogue: O /= l, lse = (m + log2 l) * ln 2, both fp32.
+// Epilogue: O /= l, lse = (m + log2 l) * ln 2, both fp32.  With bf16 weights
+//                 O is divided by l plus a correction that swaps in the
+//                 rounded weights of tiles that could dominate the row (see
+//                 rounded_sum below).
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -106,18 +105,16 @@ __device__ __forceinline__ int swz_k(int r) {
 constexpr float kTileSumLimit = 1024.0f;
 
 // bf16 weights keep 8 significant bits, so rounding one for the PV product
-// can move it by 2^-8 of itself (fp16: 2^-11).  A weight of 2^x with x > 0
-// is such a rounded value, and if its key dominates the row's softmax the
-// whole output row inherits that error (up to 2^-8 * |v|).  A weight of
-// exactly 1, the running maximum's own, is exact.  So with bf16 a tile's
-// weights are only accepted as they are while in every lane they sum to at
-// most the lane's running sum over the earlier tiles (and to kTileSumLimit);
-// otherwise m is raised to the tile's row maximum if that exceeds m, and the
-// weights are recomputed.  A weight left above 1 thus holds at most half of
-// its row.  On random data this recomputes a tile in the first few tiles of
-// a row only.  (The share is 1: measured against smaller ones, it keeps
-// random rows' recomputes to the first three tiles.)
-constexpr float kTileShareBf16 = 1.0f;
+// can move it by 2^-8 of itself (fp16: 2^-11).  If its key dominates the
+// row's softmax, O inherits that error almost whole (up to 2^-8 * |v|) when
+// the numerator sums rounded weights and the denominator l exact ones.  With
+// bf16 the kernel therefore keeps, next to l, a correction: for every tile in
+// which some lane's weights sum to more than that lane's running sum (the
+// only tiles in which a weight can hold more than half of its row), the sum
+// of the weights as rounded minus their exact sum.  O is divided by l plus
+// the correction, so such a tile's weights enter numerator and denominator
+// rounded alike and a dominant weight's rounding cancels; lse keeps the
+// exact l.  The other tiles' weights each hold at most half of their row.
 
 // Packed variable-length batches (VARLEN): q, k, v, o are [T, H, D] with
 // sequence b at rows [cu[b], cu[b+1]); lse is [H, T].
@@ -141,8 +138,8 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     constexpr int BM = C::BM, BN = C::BN, KB = C::KB, KCH = C::KCH;
     constexpr int KSTEPS = D / 16;         // QK^T MFMAs per 32-key block
     constexpr int DB = D / 32;             // 32-dim blocks of O
-    // Dominant weights kept exact (bf16 storage): see kTileShareBf16.
-    constexpr bool SHARE = std::is_same<T, BF16>::value;
+    // Normalisation by the rounded weights of dominant tiles (bf16 only).
+    constexpr bool RCORR = std::is_same<T, BF16>::value;
 
     // Two K and two V tile buffers, each its own LDS object: every access
     // below names its buffer at compile time, so the compiler can tell that
@@ -278,6 +275,7 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
+    float corr = 0.f;   // rounded minus exact weights of dominant tiles
     const floatx16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
                              0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
@@ -316,6 +314,7 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
+        corr *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -347,14 +346,33 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
             pb[kb][u][e] = (scalar)p;
         }
     };
+    // bf16: this lane's part of the tile's weight sum as rounded for the PV
+    // product (pairs summed exactly in fp32 by the dot-product instruction).
+    auto rounded_sum = [&]() __attribute__((always_inline)) {
+        float rs = 0.f;
+        if constexpr (RCORR) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const vec8 w = pb[kb][u];
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 0, 1), one, rs, false);
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 2, 3), one, rs, false);
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 4, 5), one, rs, false);
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 6, 7), one, rs, false);
+                }
+        }
+        return rs;
+    };
     // Accept the tile's weights, or (rare) raise m by the tile's largest
     // exponent (to the tile's exact row maximum), rescale O and l, shift the
     // exponents and recompute the weights.  The negated test also catches an
-    // infinite sum.  bf16 also asks when a lane's tile sum passes its running
-    // sum, and then raises only if the row maximum is above m.
+    // infinite sum.  Then, for bf16, the correction of a tile that may hold a
+    // dominant weight (see the note on bf16 weights above).
     auto accept = [&](floatx16 (&x)[KB]) __attribute__((always_inline)) {
-        const float limit = SHARE ? fminf(l_run * kTileShareBf16, kTileSumLimit) : kTileSumLimit;
-        if (__any(!(tsum <= limit))) {
+        if (__any(!(tsum <= kTileSumLimit))) {
             // Keep this a real branch: the compiler would otherwise turn it
             // into unconditional work on every tile.
             asm volatile("" ::: "memory");
@@ -366,22 +384,27 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
                     mx = __builtin_elementwise_maximum(mx, x[kb][r]);
             // delta >= 0; a lane whose keys are all masked has mx = -inf.
             const float delta = fmaxf(max_halves(mx), 0.f);
-            if (!SHARE || __any(delta > 0.f)) {
-                const float alpha = __builtin_amdgcn_exp2f(-delta);
-                m_run += delta;
-                l_run *= alpha;
+            const float alpha = __builtin_amdgcn_exp2f(-delta);
+            m_run += delta;
+            l_run *= alpha;
+            corr *= alpha;
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) x[kb][r] -= delta;
+                for (int r = 0; r < 16; ++r) x[kb][r] -= delta;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) softmax_part(x, kb, u);
+                for (int u = 0; u < 2; ++u) softmax_part(x, kb, u);
+        }
+        if constexpr (RCORR) {
+            if (__any(tsum > l_run)) {
+                asm volatile("" ::: "memory");
+                corr += rounded_sum() - tsum;
             }
         }
         l_run += tsum;
@@ -506,7 +529,7 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     // variable-length tensors) such partly written lines are evicted and
     // written back more than once.
     const float l_tot = sum_halves(l_run);
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / (RCORR ? l_tot + sum_halves(corr) : l_tot);
     if (lse != nullptr && lh == 0 && my_q < N)
         lse[lse_row0 + my_q] = (m_run + log2f(l_tot)) * kLn2;
     // Each wave stages its 32 rows, DBP dim blocks (32*DBP dims) per pass,

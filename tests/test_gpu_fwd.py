@@ -137,6 +137,48 @@ def test_running_max_raised_mid_row(orc, dtype, causal, scale_mul):
     assert_close(o.cpu().numpy(), ro, lse.cpu().numpy(), rl, f"ramped keys {dtype} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_dominant_weight_rounding_cancels(orc, causal):
+    """bf16: one key of the second tile outweighs the first tile's 64 keys
+    8-13 times over, with weights between 2^9 and 2^10 relative to the
+    running max (below the kernel's bound for raising it), so the kernel keeps them and
+    rounds each to bf16 for the PV product, off by up to 2^-8 of itself.
+    Dividing by the rounded weights of such a tile cancels most of it: with
+    w the key's weight and L = 64 + w the row sum, O's error is at most
+    2^-8 (w/L)(64/L) max|v_64 - mean(v_0..63)|, where dividing by the exact
+    sum would leave 2^-8 (w/L)|v_64|."""
+    N, d = 128, 128
+    print(f"case fwd dominant bf16 weight causal={causal}", flush=True)
+    g = torch.Generator().manual_seed(91)
+    a = torch.linspace(0.9, 1.05, N).to(torch.bfloat16)           # query i: a_i e_0
+    q = torch.zeros(1, 1, N, d, dtype=torch.bfloat16)
+    q[0, 0, :, 0] = a
+    k = torch.zeros(1, 1, N, d, dtype=torch.bfloat16)               # tile 0: scores 0
+    k[0, 0, 64, 0] = 6.4375                                          # the dominant key
+    k[0, 0, 65:, 0] = -20.0                                          # the rest of tile 1: ~0
+    v = torch.randn(1, 1, N, d, generator=g).to(torch.bfloat16)
+    v[0, 0, 64] = 4.0 * torch.sign(torch.randn(d, generator=g)).to(torch.bfloat16)
+    o, lse = fa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=1.0)
+    torch.cuda.synchronize()
+    ro, rl = orc.attention(synth.to_bits(q), synth.to_bits(k), synth.to_bits(v), "bf16", causal, 1.0)
+    og = o.cpu().numpy()
+    assert_close(og, ro, lse.cpu().numpy(), rl, f"dominant bf16 weight causal={causal}")
+    # rows that see the dominant key
+    rows = np.arange(64, N)
+    w = np.exp2(a[rows].double().numpy() * 6.4375 * math.log2(math.e))
+    assert w.min() > 256 and w.max() < 1024
+    L = 64.0 + w
+    vd = v[0, 0, 64].double().numpy()
+    spread = np.abs(vd - v[0, 0, :64].double().numpy().mean(0)).max()
+    bound = 2.0 ** -8 * (w / L) * (64.0 / L) * spread + 1e-5
+    err = np.abs(og[0, 0, rows] - ro[0, 0, rows]).max(1)
+    assert (err <= bound).all(), (err / bound).max()
+    # dividing by the exact sum would leave (w~ - w) v_64 / L: far above the bound
+    wr = torch.tensor(w).float().to(torch.bfloat16).double().numpy()
+    uncorrected = np.abs(wr - w) * np.abs(vd).max() / L
+    assert uncorrected.max() > 3 * bound.max()
+
+
 def test_single_key_returns_v(orc):
     q, k, v = synth.fwd_inputs(2, 4, 1, 128, "bf16", seed=3, device=DEV)
     o, lse = fa.fwd(q, k, v, scale=0.1)
