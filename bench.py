@@ -244,7 +244,8 @@ def ceilings(mfma_ms=10.0, launches=10):
     """What the chip sustains on each bound resource doing nothing else
     (libfa_ceiling.so): 32x32x16 16-bit MFMAs in four independent chains on
     two waves per SIMD, with N(0,1) operands (the attention inputs' values)
-    and with zero operands; and a 4 GiB stream of 16-byte loads, one
+    and with zero operands, the 16x16x32 16-bit and the FP8 products on
+    N(0,1)-like operands; and a 4 GiB stream of 16-byte loads, one
     contiguous chunk per workgroup, with the decode kernel's non-temporal
     policy and with the default one.  HIP events on the launch stream; the
     GPU's clock and power sampled during each timed loop.  One JSON line."""
@@ -286,16 +287,18 @@ def ceilings(mfma_ms=10.0, launches=10):
            "hbm_read": []}
     wg = 512                                   # two 4-wave workgroups per CU
     res = torch.empty(wg * 256, dtype=torch.float32, device=dev)
-    for dtype, data in (("fp16", "N(0,1)"), ("bf16", "N(0,1)"), ("fp16", "zeros"),
-                        ("fp8", "8 N(0,1) in E4M3")):
+    for dtype, shape, data in (("fp16", "32x32x16", "N(0,1)"), ("bf16", "32x32x16", "N(0,1)"),
+                               ("fp16", "32x32x16", "zeros"), ("fp16", "16x16x32", "N(0,1)"),
+                               ("bf16", "16x16x32", "N(0,1)"), ("fp8", "32x32x64", "8 N(0,1) in E4M3")):
         if dtype == "fp8":     # the FP8 leg's inputs: amp 8, i.e. 8 * N(0,1) rounded to E4M3
             ops = synth.fp8_inputs(1, 1, wg * 256, 64, seed=9000, device=dev)[0]
         else:
             ops = synth.normal((wg * 256 * 16,), 9000, dtype, dev)
         if data == "zeros":
             ops.zero_()
-        code = {"bf16": 0, "fp16": 1, "fp8": 2}[dtype]
-        flops_per_iter = wg * 4 * 4 * (131072.0 if dtype == "fp8" else 32768.0)
+        small = shape == "16x16x32"
+        code = {"bf16": 3 if small else 0, "fp16": 4 if small else 1, "fp8": 2}[dtype]
+        flops_per_iter = wg * 4 * 4 * (131072.0 if dtype == "fp8" else 16384.0 if small else 32768.0)
         peak = PEAK_FP8_TFLOPS if dtype == "fp8" else PEAK_MFMA_TFLOPS
         probe = 2000
         ms, _ = timed(lambda: lib.fa_ceiling_mfma(ctypes.c_void_p(ops.data_ptr()),
@@ -307,13 +310,13 @@ def ceilings(mfma_ms=10.0, launches=10):
                                                     code, sp), launches)
         tf = flops_per_iter * iters / (ms * 1e-3) / 1e12
         kname = "fa_ceiling_mfma_fp8_kernel" if dtype == "fp8" else \
-            f"fa_ceiling_mfma_kernel<{dtype.upper()}>"
-        out["mfma"].append({"kernel": kname, "dtype": dtype,
+            f"fa_ceiling_mfma{'16' if small else ''}_kernel<{dtype.upper()}>"
+        out["mfma"].append({"kernel": kname, "dtype": dtype, "shape": shape,
                             "operands": data, "iters": iters, "avg_launch_ms": round(ms, 4),
                             "achieved": round(tf, 1), "unit": "TFLOP/s",
                             "peak": peak, "frac": round(tf / peak, 4),
                             "clock_power": smi})
-        print(f"ceiling mfma {dtype} {data}: {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        print(f"ceiling mfma {dtype} {shape} {data}: {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
     nbytes = 4 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf.view(torch.int32).fill_(0x3c003c00)
@@ -622,7 +625,7 @@ def time_paged(fa, synth, stream, steps, warmup):
             "source_digest": digest}
 
 
-def cpu_baseline_all_configs(oracle_seconds=3.0):
+def cpu_baseline_all_configs(oracle_seconds=3.0, full_tensor=False):
     """The CPU-baseline leg for every workload of synth.CONFIGS (the tiny
     case, the forward benchmark shape, the key-scaled causal shape, the 128k
     causal prefill and the split-KV decode) and of the two variable-length
@@ -630,7 +633,9 @@ def cpu_baseline_all_configs(oracle_seconds=3.0):
     launch stream beside the oracle timed on the host, on the whole problem
     (tiny, decode) or on a bounded sample of rows (the three large forwards,
     extrapolated to the whole problem by its flop rate), and the error of
-    the GPU result on the oracle's rows.  One JSON line per workload.  As in
+    the GPU result on the oracle's rows.  One JSON line per workload.  With
+    full_tensor, FULL_TENSOR_CONFIG is also checked on every row of the same
+    GPU result (its line gains "parity_full_tensor").  As in
     cpu_baseline(), the oracle only serves as the baseline and the checker
     here; the GPU results come from the library alone."""
     import numpy as np
@@ -735,6 +740,11 @@ def cpu_baseline_all_configs(oracle_seconds=3.0):
                               "whole_problem_seconds": round(full_s, 1)},
                    "speedup_vs_oracle": round(full_s / (ms / 1e3)),
                    "parity": err(og, ro, lg, rl)}
+            if full_tensor and name == FULL_TENSOR_CONFIG:
+                pairs = [(b, h) for b in range(B) for h in range(H)]
+                rec["parity_full_tensor"] = check_heads(orc, qb, kb, vb, o.cpu().numpy(),
+                                                        lse.cpu().numpy(), c["dtype"], causal,
+                                                        scale, pairs)
             del q, k, v, o, lse
         torch.cuda.empty_cache()
         print(json.dumps(rec), flush=True)
@@ -831,6 +841,43 @@ def cpu_baseline_all_configs(oracle_seconds=3.0):
     print(json.dumps(rec), flush=True)
 
 
+# The workload whose rows are the most peaked (a few key rows scaled up to
+# 4x dominate them): the one --all-configs --full-tensor checks on every row.
+FULL_TENSOR_CONFIG = "causal_b4h32n16k_kscaled"
+
+
+def check_heads(orc, qb, kb, vb, og, lg, dtype, causal, scale, pairs):
+    """Errors of a forward result (og [B,H,N,d], lg [B,H,N], on the host)
+    against the oracle on every row of the (b, h) heads in `pairs`, one
+    oracle call per head, with a progress line per head on stderr."""
+    import numpy as np
+    N = og.shape[2]
+    sq_err = sq_ref = 0.0
+    max_abs = lse_abs = worst_row = 0.0
+    worst_at = None
+    odt = 0.0
+    for n, (b, h) in enumerate(pairs):
+        rows = np.stack([np.full(N, b), np.full(N, h), np.arange(N)], 1).astype(np.int64)
+        t0 = time.perf_counter()
+        ro, rl = orc.attention_rows(qb, kb, vb, dtype, rows, causal, scale)
+        odt += time.perf_counter() - t0
+        diff = og[b, h].astype(np.float64) - ro
+        sq_err += float(np.sum(diff * diff))
+        sq_ref += float(np.sum(ro * ro))
+        head_abs = float(np.abs(diff).max())
+        row_rel = np.linalg.norm(diff, axis=1) / np.maximum(np.linalg.norm(ro, axis=1), 1e-300)
+        i = int(np.argmax(row_rel))
+        if row_rel[i] > worst_row:
+            worst_row, worst_at = float(row_rel[i]), (int(b), int(h), i)
+        max_abs = max(max_abs, head_abs)
+        lse_abs = max(lse_abs, float(np.abs(lg[b, h].astype(np.float64) - rl).max()))
+        print(f"head {n + 1}/{len(pairs)} (b={b}, h={h}): max-abs {head_abs:.3e}, so far "
+              f"{max_abs:.3e}, lse {lse_abs:.3e}, oracle {odt:.0f} s", file=sys.stderr, flush=True)
+    return {"heads_checked": len(pairs), "rows_checked": len(pairs) * N,
+            "max_abs": max_abs, "rel_l2": math.sqrt(sq_err / sq_ref), "lse_max_abs": lse_abs,
+            "worst_row_rel_l2": worst_row, "worst_row": worst_at, "oracle_seconds": round(odt, 1)}
+
+
 def full_check(name, heads=None):
     """Check one forward workload of synth.CONFIGS against the oracle on
     every row of every head (or of the first `heads` heads): one fa_fwd
@@ -864,36 +911,14 @@ def full_check(name, heads=None):
     del q, k, v, o, lse
     torch.cuda.empty_cache()
     pairs = [(b, h) for b in range(B) for h in range(H)][:heads]
-    sq_err = sq_ref = 0.0
-    max_abs = lse_abs = worst_row = 0.0
-    worst_at = None
-    odt = 0.0
-    for n, (b, h) in enumerate(pairs):
-        rows = np.stack([np.full(N, b), np.full(N, h), np.arange(N)], 1).astype(np.int64)
-        t0 = time.perf_counter()
-        ro, rl = orc.attention_rows(qb, kb, vb, c["dtype"], rows, causal, scale)
-        odt += time.perf_counter() - t0
-        diff = og[b, h].astype(np.float64) - ro
-        sq_err += float(np.sum(diff * diff))
-        sq_ref += float(np.sum(ro * ro))
-        head_abs = float(np.abs(diff).max())
-        row_rel = np.linalg.norm(diff, axis=1) / np.maximum(np.linalg.norm(ro, axis=1), 1e-300)
-        i = int(np.argmax(row_rel))
-        if row_rel[i] > worst_row:
-            worst_row, worst_at = float(row_rel[i]), (b, h, i)
-        max_abs = max(max_abs, head_abs)
-        lse_abs = max(lse_abs, float(np.abs(lg[b, h].astype(np.float64) - rl).max()))
-        print(f"head {n + 1}/{len(pairs)} (b={b}, h={h}): max-abs {head_abs:.3e}, so far "
-              f"{max_abs:.3e}, lse {lse_abs:.3e}, oracle {odt:.0f} s", file=sys.stderr, flush=True)
+    res = check_heads(orc, qb, kb, vb, og, lg, c["dtype"], causal, scale, pairs)
     rec = {"full_check": name,
            "shape": f"fwd B{B} H{H} N{N} d{d} {c['dtype']} "
                     f"{'causal' if causal else 'non-causal'}"
                     + (" K rows x U[0.5,4]" if c.get("krow_scale") else ""),
-           "heads_checked": len(pairs), "rows_checked": len(pairs) * N,
-           "max_abs": max_abs, "rel_l2": math.sqrt(sq_err / sq_ref), "lse_max_abs": lse_abs,
-           "worst_row_rel_l2": worst_row, "worst_row": worst_at,
+           **{k: v for k, v in res.items() if k != "oracle_seconds"},
            "bars": {"max_abs": 2e-2, "rel_l2": 5e-3, "lse_max_abs": 1e-3},
-           "oracle": {"seconds": round(odt, 1), "cores": threads}}
+           "oracle": {"seconds": res["oracle_seconds"], "cores": threads}}
     print(json.dumps(rec), flush=True)
 
 
@@ -923,6 +948,9 @@ def main():
                          "key-scaled causal, 128k causal, decode, varlen batch, paged decode) "
                          "with its oracle time and parity on the oracle's rows, one JSON line "
                          "each")
+    ap.add_argument("--full-tensor", action="store_true",
+                    help=f"with --all-configs: also check {FULL_TENSOR_CONFIG} on every row "
+                         "(about 12 minutes of oracle time on 16 host threads)")
     ap.add_argument("--full-check", metavar="WORKLOAD", default=None,
                     help="instead of the step: check one forward workload (e.g. "
                          "causal_b4h32n16k_kscaled) against the oracle on every row")
@@ -965,7 +993,7 @@ def main():
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     if args.all_configs:
-        cpu_baseline_all_configs()
+        cpu_baseline_all_configs(full_tensor=args.full_tensor)
         return
     if args.full_check:
         full_check(args.full_check, args.heads)

@@ -35,6 +35,38 @@ __global__ __launch_bounds__(256, 2) void fa_ceiling_mfma_kernel(const u32x4 *__
     out[lane] = s;
 }
 
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(f16x8 a, f16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// The same loop on the 16x16x32 16-bit product, which does half the work of
+// a 32x32x16 one per instruction on the same operand registers but reads and
+// writes a quarter of the accumulator: whether that moves the power-limited
+// throughput decides between the two shapes for the forward's products.
+template <typename T>
+__global__ __launch_bounds__(256, 2) void fa_ceiling_mfma16_kernel(const u32x4 *__restrict__ ops,
+                                                                    float *__restrict__ out,
+                                                                    int iters) {
+    typedef typename T::vec8 vec8;
+    const size_t lane = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const vec8 a = as_vec8<vec8>(ops[2 * lane]);
+    const vec8 b = as_vec8<vec8>(ops[2 * lane + 1]);
+    floatx4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0;
+    for (int i = 0; i < iters; ++i) {
+        c0 = mfma16(a, b, c0);
+        c1 = mfma16(b, a, c1);
+        c2 = mfma16(a, a, c2);
+        c3 = mfma16(b, b, c3);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s += (c0[r] + c1[r]) + (c2[r] + c3[r]);
+    out[lane] = s;
+}
+
 // The same loop on the FP8 product of the FP8 forward,
 // v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 operands with neutral block
 // scales (twice the flops of the 16-bit product per instruction).
@@ -95,11 +127,17 @@ extern "C" {
 
 int fa_ceiling_mfma(const void *operands, float *out, int workgroups, int iters, int dtype,
                     hipStream_t stream) {
-    if (!operands || !out || workgroups < 1 || iters < 1 || dtype < 0 || dtype > 2 ||
+    if (!operands || !out || workgroups < 1 || iters < 1 || dtype < 0 || dtype > 4 ||
         (reinterpret_cast<uintptr_t>(operands) & 15))
         return (int)hipErrorInvalidValue;
     const fa::u32x4 *ops = static_cast<const fa::u32x4 *>(operands);
-    if (dtype == 2)
+    if (dtype == 4)
+        hipLaunchKernelGGL(fa::fa_ceiling_mfma16_kernel<fa::FP16>, dim3(workgroups), dim3(256), 0,
+                           stream, ops, out, iters);
+    else if (dtype == 3)
+        hipLaunchKernelGGL(fa::fa_ceiling_mfma16_kernel<fa::BF16>, dim3(workgroups), dim3(256), 0,
+                           stream, ops, out, iters);
+    else if (dtype == 2)
         hipLaunchKernelGGL(fa::fa_ceiling_mfma_fp8_kernel, dim3(workgroups), dim3(256), 0,
                            stream, ops, out, iters);
     else if (dtype == 1)

@@ -6,7 +6,8 @@
  * Nothing here is part of the attention path.
  *
  *  - The matrix-core ceiling: waves that do nothing but 32x32x16 16-bit
- *    MFMAs (the instruction both products of the forward use) on operands
+ *    MFMAs (the instruction both products of the forward use), or the
+ *    16x16x32 and FP8 products, on operands
  *    taken from memory once, so the values the matrix cores multiply have
  *    the statistics of real inputs (power draw depends on them).
  *  - The HBM read ceiling: a grid-stride stream of 16-byte loads over a
@@ -34,8 +35,10 @@ extern "C" {
  *   dtype 1: v_mfma_f32_32x32x16_f16,  4 * 32768 * iters flops per wave
  *   dtype 2: v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 (block scales 1),
  *            4 * 131072 * iters flops per wave
- *   operands : each lane's A and B operand, 32 bytes per lane (dtypes 0, 1)
- *              or 64 bytes per lane (dtype 2), workgroups * 256 lanes,
+ *   dtype 3: v_mfma_f32_16x16x32_bf16, 4 * 16384 * iters flops per wave
+ *   dtype 4: v_mfma_f32_16x16x32_f16,  4 * 16384 * iters flops per wave
+ *   operands : each lane's A and B operand, 32 bytes per lane (dtypes 0, 1,
+ *              3, 4) or 64 bytes per lane (dtype 2), workgroups * 256 lanes,
  *              16-byte aligned
  *   out      : workgroups * 256 floats (a checksum per lane, written)
  *   workgroups >= 1, iters >= 1

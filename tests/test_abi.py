@@ -311,7 +311,7 @@ def test_ceiling_library_exports_and_rejects():
     bad = 1                                               # hipErrorInvalidValue
     assert C.fa_ceiling_mfma(None, A, 1, 1, 1, None) == bad
     assert C.fa_ceiling_mfma(A, A, 0, 1, 1, None) == bad
-    assert C.fa_ceiling_mfma(A, A, 1, 1, 3, None) == bad
+    assert C.fa_ceiling_mfma(A, A, 1, 1, 5, None) == bad
     assert C.fa_ceiling_mfma(A, A, 1, 1, -1, None) == bad
     assert C.fa_ceiling_mfma(MIS, A, 1, 1, 1, None) == bad
     assert C.fa_ceiling_read(A, 0, A, 1, 1, None) == bad

@@ -22,7 +22,8 @@ def test_help_lists_the_modes():
     r = run("--help")
     assert r.returncode == 0
     for flag in ("--steps", "--warmup", "--all-configs", "--calibrate-copy", "--only",
-                 "--full-check", "--trace-summary", "--ceilings", "--sustain-s"):
+                 "--full-check", "--full-tensor", "--trace-summary", "--ceilings", "--sustain-s",
+                 "--counter-summary", "--counter-table"):
         assert flag in r.stdout
 
 
@@ -99,3 +100,30 @@ def test_counter_table_medians_per_dispatch(tmp_path):
     assert rec[0]["dispatches"] == 3
     # durations of every dispatch of both passes: 2, 4, 3 and 1 us
     assert rec[0]["time_us"] == 2.5
+
+
+def test_check_heads_measures_every_row():
+    """bench.check_heads (the full-tensor check of --full-check and
+    --all-configs --full-tensor) against a result whose errors are planted
+    on the host: one element of O and one lse of the second head."""
+    import importlib.util
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    from flashattention_attention_fa_amd import synth
+    from oracle import oracle as oracle_mod
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    orc = oracle_mod.get()
+    B, H, N, d = 1, 2, 40, 16
+    q, k, v = synth.fwd_inputs(B, H, N, d, "bf16", seed=5)
+    qb, kb, vb = synth.to_bits(q), synth.to_bits(k), synth.to_bits(v)
+    ro, rl = orc.attention(qb, kb, vb, "bf16", True, 0.25)
+    og, lg = ro.astype(np.float32), rl.astype(np.float32)
+    og[0, 1, 17, 3] += 0.01
+    lg[0, 1, 30] -= 0.002
+    res = bench.check_heads(orc, qb, kb, vb, og, lg, "bf16", True, 0.25, [(0, 0), (0, 1)])
+    assert res["heads_checked"] == 2 and res["rows_checked"] == 2 * N
+    assert abs(res["max_abs"] - 0.01) < 1e-5
+    assert abs(res["lse_max_abs"] - 0.002) < 1e-5
+    assert res["worst_row"] == (0, 1, 17)
