@@ -26,11 +26,18 @@ constexpr float kLn2 = 0.6931471805599453f;
 // (column = lane%32); lanes 32..63 hold the second half of the 16-wide
 // contraction.  C: lane%32 is the column, register r of lane half h is row
 // 8*(r/4) + 4*h + r%4.
+// mfma16: D = A*B + C on one 16x16x32 tile (v_mfma_f32_16x16x32_*), same
+// operand registers: lane group g = lane/16 holds contraction elements
+// 8g..8g+7 of A row lane%16 and of B column lane%16; C: lane%16 is the
+// column, register r is row 4g + r.
 struct BF16 {
     typedef bf16x8 vec8;
     typedef __bf16 scalar;
     static __device__ __forceinline__ floatx16 mfma32(vec8 a, vec8 b, floatx16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ floatx4 mfma16(vec8 a, vec8 b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
 };
 
@@ -39,6 +46,9 @@ struct FP16 {
     typedef _Float16 scalar;
     static __device__ __forceinline__ floatx16 mfma32(vec8 a, vec8 b, floatx16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ floatx4 mfma16(vec8 a, vec8 b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
 };
 
@@ -122,6 +132,22 @@ __device__ __forceinline__ float max_halves(float x) {
 }
 __device__ __forceinline__ float sum_halves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// max / sum over the four lane groups l, l^16, l^32, l^48 (the lanes that
+// hold one column of a 16x16 MFMA result): the halves first, then
+// v_permlane16_swap, which exchanges lane groups 0 and 1, and 2 and 3.
+__device__ __forceinline__ float max_quarters(float x) {
+    const float y = max_halves(x);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y),
+                                                    false, false);
+    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_quarters(float x) {
+    const float y = sum_halves(x);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y),
                                                     false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }

@@ -21,11 +21,14 @@
 // exponentials of tile j, then the PV MFMAs of tile j next to the exponents
 // (c*s - m) of tile j+1, so that both MFMA phases carry vector work.
 //
-// Per wave and tile (32 queries x 64 keys):
-//   S^T = K Q^T   MFMA 32x32x16; Q lives in registers for the whole loop
-//                 (B operand), K rows come from LDS (A operand).  Each lane
-//                 owns the scores of ONE query (its column): row max and row
-//                 sum are in-lane plus one swap with the other lane half.
+// Per wave and tile (32 queries x 64 keys), on 16x16x32 MFMAs:
+//   S^T = K Q^T   4 key blocks x 2 query blocks of 16x16, contraction over
+//                 the head dim in steps of 32; Q lives in registers for the
+//                 whole loop (B operand), K rows come from LDS (A operand,
+//                 each read serves both query blocks).  A lane holds 16
+//                 scores of each of TWO queries; the four lane groups that
+//                 share a query combine their maxima and sums with two lane
+//                 swaps, needed only at the end and on the rare path.
 //   online softmax in the exp2 domain with c = scale*log2(e):
 //                 m' = max(m, c*max_j s_j);  alpha = 2^(m - m');
 //                 p_j = 2^(c*s_j - m');  l = alpha*l + sum p_j;  O *= alpha
@@ -35,8 +38,14 @@
 //                 weights recomputed).  Any m that keeps the weights finite
 //                 gives the same O and lse; the bound keeps them small.
 //   O^T += V^T P^T  P^T is the S^T accumulator converted to 16 bits in
-//                 place; V^T comes from the row-major V tile through the
-//                 transposing LDS read.
+//                 place: two score blocks make one 32-key contraction (the
+//                 key order inside it is the accumulator's, matched by the V
+//                 operand); V^T comes from the V tile through the transposing
+//                 LDS read.
+// The 16x16x32 product reads and writes a quarter of the accumulator per
+// instruction that the 32x32x16 one does, for half its work: measured alone
+// on MI355X, under the board's power limit, it sustains 6 % more fp16 and
+// 3 % more bf16 throughput, and the forward follows.
 // Epilogue: O /= l, lse = (m + log2 l) * ln 2, both fp32.  With bf16 weights
 //                 O is divided by l plus a correction that swaps in the
 //                 rounded weights of tiles that could dominate the row (see
@@ -78,17 +87,17 @@ struct FwdTile {
 
 // LDS tiles are unpadded: a direct copy writes 1 KB contiguous per wave
 // instruction, 16 bytes per lane, each lane from any global address.
-//  K tile, row-major, read 16 bytes per lane with 32 consecutive rows per
-//    instruction.  Chunk c of row r is stored at chunk position c ^ swz_k(r);
+//  K tile, row-major, read 16 bytes per lane, 16 consecutive rows per
+//    16-lane group.  Chunk c of row r is stored at chunk position c ^ swz_k(r);
 //    swz_k = (r / ROWS_PER_LINE) % KCH spreads 16 consecutive rows over all
 //    16 chunk positions of a bank line.
-//  V tile, in 64-byte slabs: slab (q, r) holds dims 32q..32q+31 of key row r,
-//    at element (q * BN + r) * 32.  The transposing read takes 4 consecutive
-//    rows x 32 bytes per 16 lanes, 4 rows x 64 bytes per half wave: four
-//    consecutive slabs, i.e. 256 bytes on distinct banks.  Every read address
-//    is one per-lane register plus a compile-time offset (dim block, key
-//    block), where a row-major tile with a row swizzle needs one register
-//    per dim block.
+//  V tile, in 32-byte slabs: slab (q, r) holds dims 16q..16q+15 of key row
+//    r, at element (q * BN + r) * 16.  A transposing read takes 4 rows x 32
+//    bytes per 16 lanes and 16 consecutive rows per wave: 16 consecutive
+//    slabs, 512 contiguous bytes, each half wave on distinct banks.  Every
+//    read address is one per-lane register plus a compile-time offset (dim
+//    block, key step), where a row-major tile with a row swizzle needs one
+//    register per dim block.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
     constexpr int KCH = D / 8, ROWS_PER_LINE = 16 / KCH;
@@ -135,9 +144,12 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
                   "launch bounds must match the tile shape");
     typedef typename T::vec8 vec8;
     typedef typename T::scalar scalar;
-    constexpr int BM = C::BM, BN = C::BN, KB = C::KB, KCH = C::KCH;
-    constexpr int KSTEPS = D / 16;         // QK^T MFMAs per 32-key block
-    constexpr int DB = D / 32;             // 32-dim blocks of O
+    constexpr int BM = C::BM, BN = C::BN, KCH = C::KCH;
+    constexpr int KB = BN / 16;            // 16-key blocks per tile
+    constexpr int QB = 2;                  // 16-query blocks per wave
+    constexpr int KST = D / 32;            // QK^T MFMAs per (key block, query block)
+    constexpr int DB = D / 16;             // 16-dim blocks of O
+    constexpr int PS = BN / 32;            // PV MFMAs per (dim block, query block)
     // Normalisation by the rounded weights of dominant tiles (bf16 only).
     constexpr bool RCORR = std::is_same<T, BF16>::value;
 
@@ -152,8 +164,8 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int li = lane & 31;   // query column inside the wave's 32
-    const int lh = lane >> 5;   // lane half
+    const int li = lane & 15;   // column (query) inside a 16-query block
+    const int lg = lane >> 4;   // lane group: rows 4lg..4lg+3 of each 16-row block
 
     // Block -> (head, q-tile).  Consecutive logical ids walk the q-tiles of
     // one head, so the workgroups resident on one XCD share that head's K/V
@@ -190,19 +202,23 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     const uint32_t head_bytes = (uint32_t)((N > 0 ? (size_t)(N - 1) * RS + D : 0) * 2);
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + head, head_bytes);
     const int qw = q0 + wave * 32;    // first query of this wave
-    const int my_q = qw + li;
-
-    // Q fragments: B operand, lane (li, lh) holds query my_q, dims
-    // 16t+8lh..+8 (rows past N read as zero).
-    vec8 qf[KSTEPS];
+    int my_q[QB];                     // this lane's queries (column li of each block)
 #pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
-        u32x4 x = buffer_load16(qr, (uint32_t)(my_q * RS + 16 * t + 8 * lh) * 2u);
-        // scale < 0: flip the sign of q (exact) and use |scale|;
-        // scale == 0: every visible score is 0, i.e. q = 0.
-        x = (x & qand) ^ qxor;
-        qf[t] = as_vec8<vec8>(x);
-    }
+    for (int qb = 0; qb < QB; ++qb) my_q[qb] = qw + 16 * qb + li;
+
+    // Q fragments: B operand of block qb, step t: lane (li, lg) holds query
+    // my_q[qb], dims 32t+8lg..+8 (rows past N read as zero).
+    vec8 qf[QB][KST];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int t = 0; t < KST; ++t) {
+            u32x4 x = buffer_load16(qr, (uint32_t)(my_q[qb] * RS + 32 * t + 8 * lg) * 2u);
+            // scale < 0: flip the sign of q (exact) and use |scale|;
+            // scale == 0: every visible score is 0, i.e. q = 0.
+            x = (x & qand) ^ qxor;
+            qf[qb][t] = as_vec8<vec8>(x);
+        }
 
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int ntiles = (kv_end + BN - 1) / BN;
@@ -211,11 +227,18 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     // instruction n = wave*LOADS + i of a tile fills elements
     // [512n, 512n + 512) of its buffer.  K: rows [RPI*n, RPI*(n+1)); lane l
     // fills chunk position l%KCH of its row with the source chunk that the
-    // swizzle puts there.  V: slabs [16n, 16n + 16); lane l fills a quarter
-    // of slab 16n + l/4.  Rows past N read as zero (buffer range check) and
-    // are masked out of the softmax; tiles past the last one are copied the
-    // same way and never read.
+    // swizzle puts there.  V: 32-byte slabs [32n, 32n + 32); lane l fills
+    // half l%2 of slab 32n + l/2, and slab s holds dims 16(s/BN)..+16 of key
+    // row s%BN.  Rows past N read as zero (buffer range check) and are
+    // masked out of the softmax; tiles past the last one are copied the same
+    // way and never read.
     static_assert(C::RPI * D == 512, "one copy instruction fills 512 elements");
+    // V: instruction n reads rows 32(n%2) + lane/2 of dim block n/2.  With
+    // the packed layout's run-time row stride, its per-lane offset is kept
+    // as one register (voff0) plus a uniform part that goes into the
+    // instruction's buffer resource; with the dense layout the offsets are
+    // cheap to keep per instruction.
+    static_assert(BN == 64, "two V copy instructions per dim block");
     uint32_t koff[C::LOADS], voff[C::LOADS];
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
@@ -223,15 +246,18 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
         const int row = n * C::RPI + lane / KCH;
         const int pos = lane % KCH;
         koff[i] = (uint32_t)(row * RS + 8 * (pos ^ swz_k<D>(row))) * 2u;
-        const int slab = 16 * n + lane / 4;
-        const int vq = slab / BN, vrow = slab % BN;
-        voff[i] = (uint32_t)(vrow * RS + 32 * vq + 8 * (lane % 4)) * 2u;
+        voff[i] = (uint32_t)((32 * (n % 2) + lane / 2) * RS + 16 * (n / 2) + 8 * (lane % 2)) * 2u;
     }
+    const uint32_t voff0 = (uint32_t)((lane / 2) * RS + 8 * (lane % 2)) * 2u;
+    auto vpart = [&](int i) __attribute__((always_inline)) {
+        const int n = wave * C::LOADS + i;
+        return (uint32_t)((n % 2) * 32 * RS + 16 * (n / 2)) * 2u;
+    };
     // The tile's base goes into the (scalar) buffer resource, so the
     // per-lane offsets stay fixed and the range check still covers the end of
     // the head: a resource past the end has zero records and reads zeros.
-    auto tile_rsrc = [&](const uint16_t *base, int tile) __attribute__((always_inline)) {
-        const uint32_t off = (uint32_t)tile * (uint32_t)(BN * RS * 2);
+    auto tile_rsrc = [&](const uint16_t *base, int tile, uint32_t extra = 0u) __attribute__((always_inline)) {
+        const uint32_t off = (uint32_t)tile * (uint32_t)(BN * RS * 2) + extra;
         const uint64_t addr = (uint64_t)(uintptr_t)base + off;
         // Uniform values: keep the resource in scalar registers.
         const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
@@ -246,123 +272,127 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
             buffer_load16_lds(r, koff[i], buf + 512 * (wave * C::LOADS + i));
     };
     auto load_v = [&](int tile, uint16_t *buf) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t r = tile_rsrc(v + head, tile);
+        if constexpr (VARLEN) {
 #pragma unroll
-        for (int i = 0; i < C::LOADS; ++i)
-            buffer_load16_lds(r, voff[i], buf + 512 * (wave * C::LOADS + i));
+            for (int i = 0; i < C::LOADS; ++i)
+                buffer_load16_lds(tile_rsrc(v + head, tile, vpart(i)), voff0,
+                                  buf + 512 * (wave * C::LOADS + i));
+        } else {
+            const __amdgpu_buffer_rsrc_t r = tile_rsrc(v + head, tile);
+#pragma unroll
+            for (int i = 0; i < C::LOADS; ++i)
+                buffer_load16_lds(r, voff[i], buf + 512 * (wave * C::LOADS + i));
+        }
     };
 
-    // K operand of block kb, step t: logical chunk 2t + lh of row 32kb + li.
-    int kcol[KSTEPS];
+    // K operand of key block kb, step t: lane (li, lg) holds key row
+    // 16kb + li, logical chunk 4t + lg.  The swizzle of row 16kb + li
+    // depends on li only, so one register per step serves every key block.
+    int kcol[KST];
 #pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) kcol[t] = li * D + 8 * ((2 * t + lh) ^ swz_k<D>(li));
+    for (int t = 0; t < KST; ++t) kcol[t] = li * D + 8 * ((4 * t + lg) ^ swz_k<D>(li));
     auto read_k = [&](const uint16_t *buf, int kb, int t) __attribute__((always_inline)) {
-        return as_vec8<vec8>(*(const u32x4 *)(buf + 32 * kb * D + kcol[t]));
+        return as_vec8<vec8>(*(const u32x4 *)(buf + 16 * kb * D + kcol[t]));
     };
-    // V^T operand of PV MFMA (kb, u, db) by two transposing reads: lane j of
-    // each 16-lane group points at row 32kb + 16u + 4lh + j/4 (+8 for the
-    // second read) and dim 32db + 16*(group&1) + 4*(j%4), i.e. slab
-    // (db, row), element 16*(group&1) + 4*(j%4).
-    const int vlane = (4 * lh + ((lane & 15) >> 2)) * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    auto read_v = [&](const uint16_t *buf, int kb, int u, int db) __attribute__((always_inline)) {
-        const uint16_t *p = buf + (db * BN + 32 * kb + 16 * u) * 32 + vlane;
-        return join8<vec8>(lds_read_tr4(p), lds_read_tr4(p + 8 * 32));
+    // V^T operand of PV MFMA (db, s): contraction element e of lane group lg
+    // is key 32s + 16(e/4) + 4lg + e%4, the key the P operand below puts
+    // there.  Two transposing reads: lane j of group lg points at row
+    // 32s + 16h + 4lg + j/4 (read h) and dims 16db + 4(j%4) of slab
+    // (db, row), and receives dim 16db + j of its group's four rows.  The 16
+    // rows of one read are 16 consecutive slabs, 512 contiguous bytes.
+    const int vlane = (4 * lg + (li >> 2)) * 16 + 4 * (li & 3);
+    auto read_v = [&](const uint16_t *buf, int db, int s) __attribute__((always_inline)) {
+        const uint16_t *p = buf + (db * BN + 32 * s) * 16 + vlane;
+        return join8<vec8>(lds_read_tr4(p), lds_read_tr4(p + 16 * 16));
     };
 
-    floatx16 oacc[DB];
+    floatx4 oacc[DB][QB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-    float corr = 0.f;   // rounded minus exact weights of dominant tiles
-    const floatx16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
-                             0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m_run[QB], l_run[QB], corr[QB];   // corr: rounded minus exact weights of dominant tiles
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; corr[qb] = 0.f; }
+    const floatx4 zero4v = {0.f, 0.f, 0.f, 0.f};
 
     // S^T of one tile, two register sets used alternately (tile parity):
-    // lane (li, lh), register r of block kb holds the score of query my_q
-    // against key tile*BN + 32kb + 8(r/4) + 4lh + r%4.
-    floatx16 sA[KB], sB[KB];
+    // lane (li, lg), register r of block (kb, qb) holds the score of query
+    // my_q[qb] against key tile*BN + 16kb + 4lg + r.
+    floatx4 sA[KB][QB], sB[KB][QB];
 
     // Keys past the end and (causal) keys after the query get -inf.
-    auto mask = [&](floatx16 (&x)[KB], int tile) __attribute__((always_inline)) {
+    auto mask = [&](floatx4 (&x)[KB][QB], int tile) __attribute__((always_inline)) {
         const int kv0 = tile * BN;
-        const int lim = CAUSAL ? min(N - 1, my_q) : N - 1;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int qb = 0; qb < QB; ++qb) {
+            const int lim = CAUSAL ? min(N - 1, my_q[qb]) : N - 1;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (key > lim) x[kb][r] = -INFINITY;
-            }
-    };
-    // Row maximum of a tile in log2 units.  (maximum, not fmaxf: no NaN can
-    // occur here, and maximum maps onto v_maximum3_f32 without
-    // canonicalising every MFMA result first.)
-    float mt = 0.f;
-    auto row_max = [&](const floatx16 (&x)[KB]) __attribute__((always_inline)) {
-        float mx = __builtin_elementwise_maximum(x[0][0], x[0][1]);
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = kb == 0 ? 2 : 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, x[kb][r]);
-        mt = max_halves(mx) * c;
-    };
-    // m' = max(m, tile max); O and l scaled by 2^(m - m').
-    auto raise_max = [&]() __attribute__((always_inline)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-        corr *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    };
-
-    // P^T operands: register r of block kb becomes element r%8 of operand
-    // pb[kb][r/8]; PV MFMA (kb, u) contracts over keys
-    // 32kb + 16u + 8(e/4) + 4lh + e%4.
-    vec8 pb[KB][2];
-    // The softmax reads a tile's scores as exponents x = c*s - m, formed in
-    // place by shift() while the previous tile's PV MFMAs run (the vector
-    // ALU is otherwise idle there; this moves one of the four vector
-    // instructions per score out of the exponential phase).  m is finite
-    // from tile 0 on (every query sees key 0), so x never involves an
-    // infinite base.  tsum collects this lane's part of the tile's row sum,
-    // from the fp32 weights (the 16-bit rounding of P, up to 2^-8 relative
-    // for bf16 and 2^-11 for fp16, stays out of l and lse).
-    auto shift = [&](floatx16 (&x)[KB], int kb, int r) __attribute__((always_inline)) {
-        x[kb][r] = fmaf(x[kb][r], c, -m_run);
-    };
-    float tsum = 0.f;
-    auto softmax_part = [&](const floatx16 (&x)[KB], int kb, int u) __attribute__((always_inline)) {
-        if (kb == 0 && u == 0) tsum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(x[kb][8 * u + e]);
-            tsum += p;
-            pb[kb][u][e] = (scalar)p;
+                for (int r = 0; r < 4; ++r) {
+                    const int key = kv0 + 16 * kb + 4 * lg + r;
+                    if (key > lim) x[kb][qb][r] = -INFINITY;
+                }
         }
     };
-    // bf16: this lane's part of the tile's weight sum as rounded for the PV
+    // Largest of x over this lane's values of block qb and the three other
+    // lane groups holding the same query.  (maximum, not fmaxf: no NaN can
+    // occur here, and maximum maps onto v_maximum3_f32.)
+    auto row_max = [&](const floatx4 (&x)[KB][QB], int qb) __attribute__((always_inline)) {
+        float mx = __builtin_elementwise_maximum(x[0][qb][0], x[0][qb][1]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = kb == 0 ? 2 : 0; r < 4; ++r) mx = __builtin_elementwise_maximum(mx, x[kb][qb][r]);
+        return max_quarters(mx);
+    };
+    auto rescale = [&](int qb, float alpha) __attribute__((always_inline)) {
+        l_run[qb] *= alpha;
+        corr[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+    };
+
+    // P^T operands: pb[s][qb] element e is the weight of key
+    // 32s + 16(e/4) + 4lg + e%4, i.e. register e%4 of score block 2s + e/4.
+    vec8 pb[PS][QB];
+    // The softmax reads a tile's scores as exponents x = c*s - m, formed in
+    // place by shift() while the previous tile's PV MFMAs run (the vector
+    // ALU is otherwise idle there).  m is finite from tile 0 on (every query
+    // sees key 0), so x never involves an infinite base.  tsum collects this
+    // lane's part of the tile's row sums, from the fp32 weights (the 16-bit
+    // rounding of P, up to 2^-8 relative for bf16 and 2^-11 for fp16, stays
+    // out of l and lse).
+    auto shift = [&](floatx4 (&x)[KB][QB], int idx) __attribute__((always_inline)) {
+        const int kb = idx / (4 * QB), qb = (idx / 4) % QB, r = idx % 4;
+        x[kb][qb][r] = fmaf(x[kb][qb][r], c, -m_run[qb]);
+    };
+    float tsum[QB];
+    auto softmax_part = [&](const floatx4 (&x)[KB][QB], int kb, int qb) __attribute__((always_inline)) {
+        if (kb == 0) tsum[qb] = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(x[kb][qb][r]);
+            tsum[qb] += p;
+            pb[kb / 2][qb][4 * (kb % 2) + r] = (scalar)p;
+        }
+    };
+    // bf16: this lane's part of block qb's weight sum as rounded for the PV
     // product (pairs summed exactly in fp32 by the dot-product instruction).
-    auto rounded_sum = [&]() __attribute__((always_inline)) {
+    auto rounded_sum = [&](int qb) __attribute__((always_inline)) {
         float rs = 0.f;
         if constexpr (RCORR) {
             typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
             const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const vec8 w = pb[kb][u];
-                    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 0, 1), one, rs, false);
-                    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 2, 3), one, rs, false);
-                    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 4, 5), one, rs, false);
-                    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 6, 7), one, rs, false);
-                }
+            for (int s = 0; s < PS; ++s) {
+                const vec8 w = pb[s][qb];
+                rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 0, 1), one, rs, false);
+                rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 2, 3), one, rs, false);
+                rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 4, 5), one, rs, false);
+                rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 6, 7), one, rs, false);
+            }
         }
         return rs;
     };
@@ -371,43 +401,34 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     // exponents and recompute the weights.  The negated test also catches an
     // infinite sum.  Then, for bf16, the correction of a tile that may hold a
     // dominant weight (see the note on bf16 weights above).
-    auto accept = [&](floatx16 (&x)[KB]) __attribute__((always_inline)) {
-        if (__any(!(tsum <= kTileSumLimit))) {
+    auto accept = [&](floatx4 (&x)[KB][QB]) __attribute__((always_inline)) {
+        if (__any(!(tsum[0] <= kTileSumLimit) || !(tsum[1] <= kTileSumLimit))) {
             // Keep this a real branch: the compiler would otherwise turn it
             // into unconditional work on every tile.
             asm volatile("" ::: "memory");
-            float mx = __builtin_elementwise_maximum(x[0][0], x[0][1]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                // delta >= 0; a query whose keys are all masked has -inf.
+                const float delta = fmaxf(row_max(x, qb), 0.f);
+                m_run[qb] += delta;
+                rescale(qb, __builtin_amdgcn_exp2f(-delta));
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) x[kb][qb] -= delta;
+            }
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int r = kb == 0 ? 2 : 0; r < 16; ++r)
-                    mx = __builtin_elementwise_maximum(mx, x[kb][r]);
-            // delta >= 0; a lane whose keys are all masked has mx = -inf.
-            const float delta = fmaxf(max_halves(mx), 0.f);
-            const float alpha = __builtin_amdgcn_exp2f(-delta);
-            m_run += delta;
-            l_run *= alpha;
-            corr *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) x[kb][r] -= delta;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) softmax_part(x, kb, u);
+                for (int qb = 0; qb < QB; ++qb) softmax_part(x, kb, qb);
         }
         if constexpr (RCORR) {
-            if (__any(tsum > l_run)) {
+            if (__any(tsum[0] > l_run[0] || tsum[1] > l_run[1])) {
                 asm volatile("" ::: "memory");
-                corr += rounded_sum() - tsum;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) corr[qb] += rounded_sum(qb) - tsum[qb];
             }
         }
-        l_run += tsum;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) l_run[qb] += tsum[qb];
     };
 
     // Tiles before n_full need no mask for any query of the workgroup: all
@@ -425,15 +446,19 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t)
-            sA[kb] = T::mfma32(read_k(K0, kb, t), qf[t], t == 0 ? zero16 : sA[kb]);
+        for (int t = 0; t < KST; ++t) {
+            const vec8 kop = read_k(K0, kb, t);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                sA[kb][qb] = T::mfma16(kop, qf[qb][t], t == 0 ? zero4v : sA[kb][qb]);
+        }
     if (n_full == 0) mask(sA, 0);
-    row_max(sA);
-    raise_max();
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+        m_run[qb] = row_max(sA, qb) * c;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) shift(sA, kb, r);
+        for (int i = 0; i < 4 * KB; ++i) shift(sA, (i / 4) * 4 * QB + qb * 4 + i % 4);
+    }
     // Iteration 0 overwrites K0; every wave must be done reading K(0).
     __syncthreads();
 
@@ -445,8 +470,8 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     // run under the other's MFMAs; inside a wave, the exponentials of tile j
     // are also independent of the QK^T MFMAs next to them.  Phase boundaries
     // are fenced so the compiler keeps that order.
-    auto iteration = [&](int j, auto par, auto mask_tag, floatx16 (&cur)[KB],
-                         floatx16 (&nxt)[KB]) __attribute__((always_inline)) {
+    auto iteration = [&](int j, auto par, auto mask_tag, floatx4 (&cur)[KB][QB],
+                         floatx4 (&nxt)[KB][QB]) __attribute__((always_inline)) {
         constexpr bool MASK_NEXT = decltype(mask_tag)::value;
         constexpr int PAR = decltype(par)::value;
         uint16_t *const kb_next = PAR ? K0 : K1;   // holds K(j+1)
@@ -456,34 +481,46 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
 
         load_k(j + 2, kb_fill);
         load_v(j + 1, vb_fill);
-        // Phase 1: QK^T(j+1) | softmax(j).
+        // Phase 1: QK^T(j+1) | softmax(j): the KB*QB softmax blocks spread
+        // over the KB*KST*QB MFMAs.
+        constexpr int NM1 = KB * KST * QB, SB1 = KB * QB;
+        static_assert(NM1 % SB1 == 0, "phase 1 spreads whole softmax blocks");
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int t = 0; t < KSTEPS; ++t) {
-                nxt[kb] = T::mfma32(read_k(kb_next, kb, t), qf[t], t == 0 ? zero16 : nxt[kb]);
-                if (t == 1) softmax_part(cur, kb, 0);
-                if (t == KSTEPS / 2 + 1) softmax_part(cur, kb, 1);
+            for (int t = 0; t < KST; ++t) {
+                const vec8 kop = read_k(kb_next, kb, t);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    nxt[kb][qb] = T::mfma16(kop, qf[qb][t], t == 0 ? zero4v : nxt[kb][qb]);
+                    const int m = (kb * KST + t) * QB + qb;
+                    if (m % (NM1 / SB1) == 0) {
+                        const int sb = m / (NM1 / SB1);
+                        softmax_part(cur, sb / QB, sb % QB);
+                    }
+                }
             }
         __builtin_amdgcn_sched_barrier(0);
         accept(cur);
         __builtin_amdgcn_sched_barrier(0);
         // Phase 2: PV(j) | mask and exponents of tile j+1, SPM scores next
-        // to each of the 2*KB*DB MFMAs.
+        // to each of the DB*PS*QB MFMAs.
         if constexpr (MASK_NEXT) mask(nxt, j + 1);
-        constexpr int SPM = 16 * KB / (2 * KB * DB);
-        static_assert(SPM * 2 * KB * DB == 16 * KB, "phase 2 must cover every score once");
+        constexpr int NM2 = DB * PS * QB, SPM = 4 * KB * QB / NM2;
+        static_assert(SPM * NM2 == 4 * KB * QB, "phase 2 must cover every score once");
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int s = 0; s < PS; ++s)
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int db = 0; db < DB; ++db) {
+                const vec8 vop = read_v(vb_cur, db, s);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    oacc[db] = T::mfma32(read_v(vb_cur, kb, u, db), pb[kb][u], oacc[db]);
-                    const int i = SPM * ((kb * 2 + u) * DB + db);
+                for (int qb = 0; qb < QB; ++qb) {
+                    oacc[db][qb] = T::mfma16(vop, pb[s][qb], oacc[db][qb]);
+                    const int i = SPM * ((s * DB + db) * QB + qb);
 #pragma unroll
-                    for (int e = 0; e < SPM; ++e) shift(nxt, (i + e) / 16, (i + e) % 16);
+                    for (int e = 0; e < SPM; ++e) shift(nxt, i + e);
                 }
+            }
         __builtin_amdgcn_sched_barrier(0);
         wait_vmem();
         __syncthreads();
@@ -504,43 +541,49 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     run(split, ntiles - 1, std::true_type{});
 
     // Last tile: softmax and PV only.
-    auto last = [&](floatx16 (&cur)[KB], const uint16_t *vb) __attribute__((always_inline)) {
+    auto last = [&](floatx4 (&cur)[KB][QB], const uint16_t *vb) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) softmax_part(cur, kb, u);
+            for (int qb = 0; qb < QB; ++qb) softmax_part(cur, kb, qb);
         accept(cur);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int s = 0; s < PS; ++s)
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int db = 0; db < DB; ++db) {
+                const vec8 vop = read_v(vb, db, s);
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    oacc[db] = T::mfma32(read_v(vb, kb, u, db), pb[kb][u], oacc[db]);
+                for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = T::mfma16(vop, pb[s][qb], oacc[db][qb]);
+            }
     };
     if ((ntiles - 1) & 1) last(sB, V1); else last(sA, V0);
 
-    // Epilogue.  O^T accumulator: lane (li, lh), register r of block db holds
-    // dim 32*db + 8*(r/4) + 4*lh + r%4 of query my_q.  O is written through
-    // LDS (the K/V tile buffers are free once every wave is past the last
-    // tile), so that each store instruction writes whole rows: straight from
-    // the accumulator, one instruction would put 32 bytes into each of 32
-    // rows, and where rows lie far apart (the H*d stride of packed
+    // Epilogue.  O^T accumulator: lane (li, lg), register r of block
+    // (db, qb) holds dim 16db + 4lg + r of query my_q[qb].  O is written
+    // through LDS (the K/V tile buffers are free once every wave is past the
+    // last tile), so that each store instruction writes whole rows: straight
+    // from the accumulator, one instruction would put 16 bytes into each of
+    // 64 rows, and where rows lie far apart (the H*d stride of packed
     // variable-length tensors) such partly written lines are evicted and
     // written back more than once.
-    const float l_tot = sum_halves(l_run);
-    const float inv = 1.f / (RCORR ? l_tot + sum_halves(corr) : l_tot);
-    if (lse != nullptr && lh == 0 && my_q < N)
-        lse[lse_row0 + my_q] = (m_run + log2f(l_tot)) * kLn2;
-    // Each wave stages its 32 rows, DBP dim blocks (32*DBP dims) per pass,
-    // in its share of one tile buffer: row r holds CPR 16-byte chunks, chunk
-    // c stored at position c ^ (r % 16), which keeps the column writes and
-    // the row reads on distinct banks.
+    float inv[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l_tot = sum_quarters(l_run[qb]);
+        inv[qb] = 1.f / (RCORR ? l_tot + sum_quarters(corr[qb]) : l_tot);
+        if (lse != nullptr && lg == 0 && my_q[qb] < N)
+            lse[lse_row0 + my_q[qb]] = (m_run[qb] + log2f(l_tot)) * kLn2;
+    }
+    // Each wave stages its 32 rows, CPR 16-byte chunks (4*CPR dims) per
+    // pass, in its share of one tile buffer: chunk c of row r is stored at
+    // position c ^ (r % 16), which keeps the column writes and the row reads
+    // on distinct banks.
     constexpr int WPB = C::WAVES / 4;                       // waves per tile buffer
-    constexpr int DBP = C::ELEMS * 2 / WPB / 4096;          // dim blocks per pass
-    constexpr int CPR = 8 * DBP;                            // chunks per staged row
+    constexpr int CPR = C::ELEMS * 2 / WPB / 32 / 16;       // chunks per staged row
     constexpr int RPI = 64 / CPR;                           // rows per store instruction
-    static_assert(DBP >= 1 && DB % DBP == 0 && 64 % CPR == 0, "staging must fit a tile buffer");
+    constexpr int NPASS = D / 4 / CPR;
+    static_assert(CPR >= 16 && CPR % 4 == 0 && NPASS * CPR * 4 == D && 64 % CPR == 0,
+                  "staging must fit a tile buffer");
     uint16_t *const sbuf = (wave % 4) == 0 ? K0 : (wave % 4) == 1 ? K1 : (wave % 4) == 2 ? V0 : V1;
     floatx4 *const stage = (floatx4 *)sbuf + (wave / 4) * 32 * CPR;
     __syncthreads();
@@ -549,18 +592,16 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     // they would stay live, and spill, across it).
     int el = lane;
     asm volatile("" : "+v"(el));
-    const int eli = el & 31;
+    const int eli = el & 15, elg = el >> 4;
 #pragma unroll
-    for (int pass = 0; pass < DB / DBP; ++pass) {
+    for (int pass = 0; pass < NPASS; ++pass) {
 #pragma unroll
-        for (int dl = 0; dl < DBP; ++dl)
+        for (int dl = 0; dl < CPR / 4; ++dl)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int db = pass * DBP + dl;
-                const int ch = 8 * dl + 2 * a + (el >> 5);
-                stage[eli * CPR + (ch ^ (eli % 16))] =
-                    floatx4{oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv,
-                            oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv};
+            for (int qb = 0; qb < QB; ++qb) {
+                const int db = pass * (CPR / 4) + dl;
+                const int row = 16 * qb + eli, ch = 4 * dl + elg;
+                stage[row * CPR + (ch ^ eli)] = oacc[db][qb] * inv[qb];
             }
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -568,7 +609,7 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
             const int r = i * RPI + el / CPR, ch = el % CPR;
             const floatx4 x = stage[r * CPR + (ch ^ (r % 16))];
             if (qw + r < N)
-                *(floatx4 *)(o + head + (size_t)(qw + r) * RS + 32 * DBP * pass + 4 * ch) = x;
+                *(floatx4 *)(o + head + (size_t)(qw + r) * RS + 4 * (CPR * pass + ch)) = x;
         }
         __builtin_amdgcn_wave_barrier();
     }
