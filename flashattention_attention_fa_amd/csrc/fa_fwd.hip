@@ -521,6 +521,18 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
                     for (int e = 0; e < SPM; ++e) shift(nxt, i + e);
                 }
             }
+        // Causal kernels: at most four V reads ahead of the PV MFMAs (left to
+        // itself the scheduler issues them all early, and these kernels,
+        // with their mask state, then spill).
+        if constexpr (CAUSAL) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < NM2 / 2 - 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
         wait_vmem();
         __syncthreads();
@@ -566,13 +578,19 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     // 64 rows, and where rows lie far apart (the H*d stride of packed
     // variable-length tensors) such partly written lines are evicted and
     // written back more than once.
+    // Packed variable-length layout: the lane index is recomputed from the
+    // execution mask, so nothing needs to carry it, or this lane's query
+    // numbers, through the loop (its kernels otherwise spilled them).
+    const int lane_e =
+        VARLEN ? (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) : lane;
     float inv[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l_tot = sum_quarters(l_run[qb]);
         inv[qb] = 1.f / (RCORR ? l_tot + sum_quarters(corr[qb]) : l_tot);
-        if (lse != nullptr && lg == 0 && my_q[qb] < N)
-            lse[lse_row0 + my_q[qb]] = (m_run[qb] + log2f(l_tot)) * kLn2;
+        const int qe = qw + 16 * qb + (lane_e & 15);
+        if (lse != nullptr && lane_e < 16 && qe < N)
+            lse[lse_row0 + qe] = (m_run[qb] + log2f(l_tot)) * kLn2;
     }
     // Each wave stages its 32 rows, CPR 16-byte chunks (4*CPR dims) per
     // pass, in its share of one tile buffer: chunk c of row r is stored at
@@ -588,9 +606,9 @@ __global__ __launch_bounds__((64 * fwd_waves<D, CAUSAL>()), (8 / fwd_waves<D, CA
     floatx4 *const stage = (floatx4 *)sbuf + (wave / 4) * 32 * CPR;
     __syncthreads();
     // The staging addresses depend on the lane only; taken from an opaque
-    // copy of it, the compiler cannot compute them before the loop (where
-    // they would stay live, and spill, across it).
-    int el = lane;
+    // copy of the recomputed lane index, the compiler cannot compute them
+    // before the loop (where they would stay live, and spill, across it).
+    int el = lane_e;
     asm volatile("" : "+v"(el));
     const int eli = el & 15, elg = el >> 4;
 #pragma unroll
