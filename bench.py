@@ -77,6 +77,12 @@ def source_digest(*names):
     return h.hexdigest()[:16]
 
 
+# roofline.traffic is not measured by the run that prints it: it is read
+# from the committed counter record of the same kernel source.
+TRAFFIC_SOURCE = ("profiles/traffic.json: rocprofv3 FETCH_SIZE + WRITE_SIZE of this kernel source "
+                  "(matched by source digest, null otherwise), not measured by this run")
+
+
 def load_traffic(kernel_key, digest, launches_per_unit=1):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None
     when absent or taken on a different kernel source."""
@@ -1127,6 +1133,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
             "traffic": fwd_traffic,
+            "traffic_source": TRAFFIC_SOURCE,
             "algorithmic_flops_per_launch": flops,
             "algorithmic_bytes_per_launch": fwd_bytes(c["B"], c["H"], c["N"], c["d"]),
             "avg_launch_ms": round(fwd_ms, 4),
@@ -1140,7 +1147,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4),
-            "traffic": dec_traffic,
+            "traffic": dec_traffic, "traffic_source": TRAFFIC_SOURCE,
             "algorithmic_bytes_per_call": dbytes,
             "avg_call_us": round(dec_ms * 1e3, 2),
             "median_call_us": round(median(dec_calls) * 1e3, 2),
