@@ -5,11 +5,11 @@
  * be read against an achievable ceiling as well as the published peak.
  * Nothing here is part of the attention path.
  *
- *  - The matrix-core ceiling: waves that do nothing but 32x32x16 16-bit
- *    MFMAs (the instruction both products of the forward use), or the
- *    16x16x32 and FP8 products, on operands
- *    taken from memory once, so the values the matrix cores multiply have
- *    the statistics of real inputs (power draw depends on them).
+ *  - The matrix-core ceiling: waves that do nothing but MFMAs of one shape
+ *    (16x16x32 16-bit, the forward's; 32x32x16 16-bit, the backward's;
+ *    32x32x64 FP8, the FP8 forward's) on operands taken from memory once,
+ *    so the values the matrix cores multiply have the statistics of real
+ *    inputs (power draw depends on them).
  *  - The HBM read ceiling: a grid-stride stream of 16-byte loads over a
  *    buffer much larger than the last-level cache, with the non-temporal
  *    policy the decode kernel uses, or the default one.
