@@ -323,6 +323,27 @@ def ceilings(mfma_ms=10.0, launches=10):
                             "peak": peak, "frac": round(tf / peak, 4),
                             "clock_power": smi})
         print(f"ceiling mfma {dtype} {shape} {data}: {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    # LDS: two 4-wave workgroups per CU, 8 reads per lane per iteration.
+    lib.fa_ceiling_lds.argtypes = [P, I, I, I, P]
+    out["lds_read"] = []
+    lds_res = torch.empty(wg * 256, dtype=torch.int32, device=dev)
+    for mode, what, per_lane in ((0, "ds_read_b128, 256 contiguous bytes per 16 lanes", 128),
+                                 (1, "ds_read_b64_tr_b16 (transposing)", 64)):
+        probe = 2000
+        ms, _ = timed(lambda: lib.fa_ceiling_lds(ctypes.c_void_p(lds_res.data_ptr()), wg, probe,
+                                                 mode, sp), 2, window_s=0.0)
+        iters = max(100, int(probe * mfma_ms / max(ms, 1e-3)))
+        ms, smi = timed(lambda: lib.fa_ceiling_lds(ctypes.c_void_p(lds_res.data_ptr()), wg, iters,
+                                                   mode, sp), launches)
+        nb = wg * 256 * per_lane * iters
+        bps = nb / (ms * 1e-3)
+        clk = smi.get("sclk_mhz", {}).get("median") if isinstance(smi, dict) else None
+        out["lds_read"].append({"kernel": f"fa_ceiling_lds_kernel<{mode}>", "read": what,
+                                "iters": iters, "avg_launch_ms": round(ms, 4),
+                                "achieved": round(bps / 1e12, 2), "unit": "TB/s",
+                                "bytes_per_clock_per_cu": round(bps / (256 * clk * 1e6), 1) if clk else None,
+                                "clock_power": smi})
+        print(f"ceiling lds mode {mode}: {bps / 1e12:.2f} TB/s", file=sys.stderr, flush=True)
     nbytes = 4 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf.view(torch.int32).fill_(0x3c003c00)

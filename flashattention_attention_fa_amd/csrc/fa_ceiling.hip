@@ -121,6 +121,44 @@ __global__ __launch_bounds__(256) void fa_ceiling_read_kernel(const unsigned cha
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
 }
 
+// LDS read bandwidth: a 64 KiB tile filled once, then read back over and
+// over with the access patterns of the attention kernels' operand reads,
+// eight independent reads in flight per wave.  MODE 0: ds_read_b128, 16
+// consecutive 16-byte chunks per 16 lanes (a row read, conflict-free);
+// MODE 1: ds_read_b64_tr_b16 (the transposing read), 512 contiguous bytes
+// per instruction.
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void fa_ceiling_lds_kernel(unsigned *__restrict__ out, int iters) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[32768];
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = (i * 256 + tid) * 8;
+        *(u32x4 *)(tile + e) = u32x4{(unsigned)e, (unsigned)e ^ 0x5555u, (unsigned)e + 7u,
+                                     (unsigned)tid};
+    }
+    __syncthreads();
+    const int wave = tid >> 6, lane = tid & 63;
+    // Each of the four waves reads its own 16 KiB quarter of the tile.
+    const int base = (wave & 3) * 8192;
+    u32x4 x = zero4();
+    for (int it = 0; it < iters; ++it) {
+        const int rot = (it & 7) * 512;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if constexpr (MODE == 0) {
+                const int e = base + ((rot + r * 1024 + lane * 8) & 8191);
+                x ^= *(const u32x4 *)(tile + e);
+            } else {
+                const int e = base + ((rot + r * 1024 + lane * 4) & 8191);
+                const shortx4 t = lds_read_tr4(tile + e);
+                x[r & 3] ^= (unsigned)(uint16_t)t[0] | ((unsigned)(uint16_t)t[3] << 16);
+            }
+        }
+    }
+    out[(size_t)blockIdx.x * 256 + tid] = x[0] ^ x[1] ^ x[2] ^ x[3];
+}
+
 }  // namespace fa
 
 extern "C" {
@@ -146,6 +184,18 @@ int fa_ceiling_mfma(const void *operands, float *out, int workgroups, int iters,
     else
         hipLaunchKernelGGL(fa::fa_ceiling_mfma_kernel<fa::BF16>, dim3(workgroups), dim3(256), 0,
                            stream, ops, out, iters);
+    return (int)hipGetLastError();
+}
+
+int fa_ceiling_lds(unsigned *out, int workgroups, int iters, int mode, hipStream_t stream) {
+    if (!out || workgroups < 1 || iters < 1 || mode < 0 || mode > 1)
+        return (int)hipErrorInvalidValue;
+    if (mode == 0)
+        hipLaunchKernelGGL(fa::fa_ceiling_lds_kernel<0>, dim3(workgroups), dim3(256), 0, stream, out,
+                           iters);
+    else
+        hipLaunchKernelGGL(fa::fa_ceiling_lds_kernel<1>, dim3(workgroups), dim3(256), 0, stream, out,
+                           iters);
     return (int)hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
 /*
- * fa_ceiling.h -- C ABI of libfa_ceiling.so: two measurement kernels that
- * show what MI355X (gfx950) sustains on the two resources the attention
+ * fa_ceiling.h -- C ABI of libfa_ceiling.so: measurement kernels that
+ * show what MI355X (gfx950) sustains on the resources the attention
  * kernels of libfa_amd.so are bound by, so that their roofline fractions can
  * be read against an achievable ceiling as well as the published peak.
  * Nothing here is part of the attention path.
@@ -10,11 +10,13 @@
  *    32x32x64 FP8, the FP8 forward's) on operands taken from memory once,
  *    so the values the matrix cores multiply have the statistics of real
  *    inputs (power draw depends on them).
+ *  - The LDS read ceiling: the operand reads of the attention kernels
+ *    (16-byte row reads, 8-byte transposing reads) from a resident tile.
  *  - The HBM read ceiling: a grid-stride stream of 16-byte loads over a
  *    buffer much larger than the last-level cache, with the non-temporal
  *    policy the decode kernel uses, or the default one.
  *
- * Both enqueue on `stream` and return hipSuccess (0) or the HIP error of the
+ * All enqueue on `stream` and return hipSuccess (0) or the HIP error of the
  * launch; arguments are checked first (hipErrorInvalidValue, nothing
  * enqueued).  All pointers are device pointers owned by the caller.
  */
@@ -45,6 +47,19 @@ extern "C" {
  */
 int fa_ceiling_mfma(const void *operands, float *out, int workgroups, int iters, int dtype,
                     hipStream_t stream);
+
+/*
+ * fa_ceiling_lds -- LDS read bandwidth: `workgroups` workgroups of 4 waves,
+ * each filling a 64 KiB LDS tile once and then reading it iters x 8 times per
+ * lane, eight independent reads in flight:
+ *   mode 0: ds_read_b128 (16 bytes per lane, 256 contiguous bytes per 16
+ *           lanes): 128 bytes per lane per iteration
+ *   mode 1: ds_read_b64_tr_b16 (8 bytes per lane): 64 bytes per lane per
+ *           iteration
+ *   out : workgroups * 256 uint32 (an XOR checksum per lane, written)
+ *   workgroups >= 1, iters >= 1
+ */
+int fa_ceiling_lds(unsigned *out, int workgroups, int iters, int mode, hipStream_t stream);
 
 /*
  * fa_ceiling_read -- reads `bytes` bytes of `src` once, 16 bytes per load:

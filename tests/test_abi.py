@@ -302,18 +302,23 @@ def test_ceiling_library_exports_and_rejects():
     text = re.sub(r"/\*.*?\*/", "", (Path(fa.HEADER_PATH).with_name("fa_ceiling.h")).read_text(),
                   flags=re.S)
     names = re.findall(r"^\s*int\s+(fa_[a-z0-9_]+)\s*\(", text, flags=re.M)
-    assert names == ["fa_ceiling_mfma", "fa_ceiling_read"]
+    assert names == ["fa_ceiling_mfma", "fa_ceiling_lds", "fa_ceiling_read"]
     for n in names:
         assert hasattr(C, n), n
     P, I = ctypes.c_void_p, ctypes.c_int
     C.fa_ceiling_mfma.argtypes = [P, P, I, I, I, P]
     C.fa_ceiling_read.argtypes = [P, ctypes.c_size_t, P, I, I, P]
+    C.fa_ceiling_lds.argtypes = [P, I, I, I, P]
     bad = 1                                               # hipErrorInvalidValue
     assert C.fa_ceiling_mfma(None, A, 1, 1, 1, None) == bad
     assert C.fa_ceiling_mfma(A, A, 0, 1, 1, None) == bad
     assert C.fa_ceiling_mfma(A, A, 1, 1, 5, None) == bad
     assert C.fa_ceiling_mfma(A, A, 1, 1, -1, None) == bad
     assert C.fa_ceiling_mfma(MIS, A, 1, 1, 1, None) == bad
+    assert C.fa_ceiling_lds(None, 1, 1, 0, None) == bad
+    assert C.fa_ceiling_lds(A, 0, 1, 0, None) == bad
+    assert C.fa_ceiling_lds(A, 1, 0, 0, None) == bad
+    assert C.fa_ceiling_lds(A, 1, 1, 2, None) == bad
     assert C.fa_ceiling_read(A, 0, A, 1, 1, None) == bad
     assert C.fa_ceiling_read(A, 24, A, 1, 1, None) == bad
     assert C.fa_ceiling_read(A, 1 << 32, A, 1, 1, None) == bad    # a 4 GiB chunk
