@@ -9,10 +9,17 @@
 // pipeline figure's FP8 note).
 //
 // Both products run on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32
-// accumulation, neutral block scales), twice the fp16 rate; the wave's
-// structure is the fp16 kernel's (32 queries per wave, two waves per SIMD,
-// 64-key tiles copied global->LDS by DMA, QK^T(j+1) pipelined next to the
-// softmax of tile j).  What changes:
+// accumulation, neutral block scales), twice the fp16 rate; 32 queries per
+// wave, two waves per SIMD, 64-key tiles copied global->LDS by DMA.  With
+// four times fewer MFMAs per score than the 16-bit kernels, this kernel is
+// bound by its vector work (exponentials, row sums, conversions), so the
+// pipeline keeps MFMAs next to that work in every wave: iteration j forms
+// the softmax of tile j between the MFMAs of QK^T(j+1) and of PV(j-1) (PV
+// trails by one tile; V(j) is copied during iteration j and read in j+1).
+// When every wave of the workgroup runs the PV MFMAs of a tile together
+// after its softmax, as the 16-bit kernels do, the per-tile barrier keeps
+// the two waves of a SIMD in step and the vector unit idles through them.
+// What else changes:
 //
 //  * S^T = K Q^T contracts 64 dims per MFMA.  Lane (i, h) of the A operand
 //    holds 32 consecutive dims of one key row; lane (j, h) of the B operand
@@ -277,9 +284,9 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_fp8
 
     // P^T operand bytes: dword w = 4kb + (r/4) of pb holds registers
     // 4(w%4) .. +3 of block kb.
-    i32x8 pb;
+    i32x8 pbA, pbB;
     float tsum = 0.f;
-    auto softmax_part = [&](const floatx16 (&x)[KB], int kb, int half) __attribute__((always_inline)) {
+    auto softmax_part = [&](const floatx16 (&x)[KB], i32x8 &pb, int kb, int half) __attribute__((always_inline)) {
         if (kb == 0 && half == 0) tsum = 0.f;
         const float bias = kPShift - m_run;
 #pragma unroll
@@ -298,7 +305,7 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_fp8
     // (the negated test also catches an infinite sum); otherwise look at the
     // tile's row maximum and, if a score passes m + kRaise, raise m to it,
     // rescale O and l, and recompute the weights.
-    auto accept = [&](const floatx16 (&x)[KB]) __attribute__((always_inline)) {
+    auto accept = [&](const floatx16 (&x)[KB], i32x8 &pb) __attribute__((always_inline)) {
         if (__any(!(tsum <= kE4M3Max))) {
             asm volatile("" ::: "memory");
             row_max(x);
@@ -307,7 +314,7 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_fp8
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) softmax_part(x, kb, h);
+                    for (int h = 0; h < 2; ++h) softmax_part(x, pb, kb, h);
             }
         }
         l_run += tsum;
@@ -318,7 +325,6 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_fp8
     n_full = min(n_full, ntiles);
 
     load_tile(k, 0, K0);
-    load_tile(v, 0, V0);
     load_tile(k, 1, K1);
     wait_vmem();
     __syncthreads();
@@ -332,60 +338,101 @@ __global__ __launch_bounds__(CAUSAL ? 256 : 512, CAUSAL ? 2 : 1) void fa_fwd_fp8
     raise_max();
     __syncthreads();
 
-    // Iteration j (parity PAR): softmax(j) next to QK^T(j+1), then PV(j),
-    // copies of K(j+2) and V(j+1) in flight meanwhile (see fa_fwd.hip).
-    auto iteration = [&](int j, auto par, auto mask_tag, floatx16 (&cur)[KB],
+    // Iteration j (parity PAR): softmax(j) next to QK^T(j+1) and PV(j-1),
+    // copies of K(j+2) and V(j) in flight meanwhile.  PV trails the softmax
+    // by one tile so that its MFMAs overlap this wave's vector work.
+    auto iteration = [&](int j, auto par, auto mask_tag, auto first_tag, floatx16 (&cur)[KB],
                          floatx16 (&nxt)[KB]) __attribute__((always_inline)) {
         constexpr bool MASK_NEXT = decltype(mask_tag)::value;
+        constexpr bool FIRST = decltype(first_tag)::value;
         constexpr int PAR = decltype(par)::value;
         uint8_t *const kb_next = PAR ? K0 : K1;
         uint8_t *const kb_fill = PAR ? K1 : K0;
-        uint8_t *const vb_cur = PAR ? V1 : V0;
-        uint8_t *const vb_fill = PAR ? V0 : V1;
+        uint8_t *const vb_prev = PAR ? V0 : V1;
+        uint8_t *const vb_fill = PAR ? V1 : V0;
+        i32x8 &pb_cur = PAR ? pbB : pbA;
+        i32x8 &pb_prev = PAR ? pbA : pbB;
 
         load_tile(k, j + 2, kb_fill);
-        load_tile(v, j + 1, vb_fill);
+        load_tile(v, j, vb_fill);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
                 nxt[kb] = mfma_fp8(read_k(kb_next, kb, t), qf[t], t == 0 ? zero16 : nxt[kb]);
-                if (t == 0) softmax_part(cur, kb, 0);
-                if (t == KT - 1) softmax_part(cur, kb, 1);
+                if (t == 0) softmax_part(cur, pb_cur, kb, 0);
+                if constexpr (!FIRST) {
+                    constexpr int PER = DB / (KB * KT) > 0 ? DB / (KB * KT) : 1;
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) {
+                        const int db = (kb * KT + t) * PER + e;
+                        if (db < DB) oacc[db] = mfma_fp8(read_v(vb_prev, db), pb_prev, oacc[db]);
+                    }
+                }
+                if (t == KT - 1) softmax_part(cur, pb_cur, kb, 1);
             }
         __builtin_amdgcn_sched_barrier(0);
-        accept(cur);
+        accept(cur, pb_cur);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (MASK_NEXT) mask(nxt, j + 1);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] = mfma_fp8(read_v(vb_cur, db), pb, oacc[db]);
-        __builtin_amdgcn_sched_barrier(0);
         wait_vmem();
         __syncthreads();
     };
+    typedef std::false_type NF;
+    typedef std::true_type YF;
     auto run = [&](int j0, int j1, auto mask_tag) __attribute__((always_inline)) {
         int j = j0;
-        if (j < j1 && (j & 1)) iteration(j++, P1{}, mask_tag, sB, sA);
+        if (j < j1 && (j & 1)) iteration(j++, P1{}, mask_tag, NF{}, sB, sA);
         for (; j + 1 < j1; j += 2) {
-            iteration(j, P0{}, mask_tag, sA, sB);
-            iteration(j + 1, P1{}, mask_tag, sB, sA);
+            iteration(j, P0{}, mask_tag, NF{}, sA, sB);
+            iteration(j + 1, P1{}, mask_tag, NF{}, sB, sA);
         }
-        if (j < j1) iteration(j, P0{}, mask_tag, sA, sB);
+        if (j < j1) iteration(j, P0{}, mask_tag, NF{}, sA, sB);
     };
     const int split = max(0, min(n_full - 1, ntiles - 1));
-    run(0, split, std::false_type{});
-    run(split, ntiles - 1, std::true_type{});
+    int j_start = 0;
+    if (ntiles > 1) {
+        if (split > 0) iteration(0, P0{}, std::false_type{}, YF{}, sA, sB);
+        else iteration(0, P0{}, std::true_type{}, YF{}, sA, sB);
+        j_start = 1;
+    }
+    run(j_start, max(j_start, split), std::false_type{});
+    run(max(j_start, split), ntiles - 1, std::true_type{});
 
-    auto last = [&](floatx16 (&cur)[KB], const uint8_t *vb) __attribute__((always_inline)) {
+    // Last tile L: V(L) copied now; softmax(L) next to PV(L-1), then PV(L).
+    auto last = [&](floatx16 (&cur)[KB], auto par, auto first_tag) __attribute__((always_inline)) {
+        constexpr bool FIRST = decltype(first_tag)::value;
+        constexpr int PAR = decltype(par)::value;
+        uint8_t *const vb_prev = PAR ? V0 : V1;
+        uint8_t *const vb_cur = PAR ? V1 : V0;
+        i32x8 &pb_cur = PAR ? pbB : pbA;
+        i32x8 &pb_prev = PAR ? pbA : pbB;
+        load_tile(v, ntiles - 1, vb_cur);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) softmax_part(cur, kb, h);
-        accept(cur);
+            for (int h = 0; h < 2; ++h) softmax_part(cur, pb_cur, kb, h);
+        if constexpr (!FIRST) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] = mfma_fp8(read_v(vb, db), pb, oacc[db]);
+            for (int db = 0; db < DB; ++db) oacc[db] = mfma_fp8(read_v(vb_prev, db), pb_prev, oacc[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        accept(cur, pb_cur);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmem();
+        __syncthreads();
+        // One V operand in flight at a time here: the registers of the
+        // pipeline are free, but the compiler would otherwise read all of
+        // V at once and spill.
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            oacc[db] = mfma_fp8(read_v(vb_cur, db), pb_cur, oacc[db]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
-    if ((ntiles - 1) & 1) last(sB, V1); else last(sA, V0);
+    if (ntiles == 1) last(sA, P0{}, YF{});
+    else if ((ntiles - 1) & 1) last(sB, P1{}, NF{});
+    else last(sA, P0{}, NF{});
 
     // Epilogue: O = vd * sum p'v / sum p'; lse = (m - kPShift + log2 l') ln 2.
     const float l_tot = sum_halves(l_run);
