@@ -132,7 +132,10 @@ def test_ragged_multi_tile(orc, causal, d):
     run_full(orc, 2, 3, 333, d, causal, seed=2010 + d)
 
 
-@pytest.mark.parametrize("N", [1, 2, 31, 63, 64, 65, 127, 129, 257])
+# Odd lengths run causal, even ones not: non-causal 96/128, 130/192 and 256
+# give rows of 2, 3 and 4 key tiles, so the pipeline's first iteration, its
+# last tile and both parities of its loop are exercised.
+@pytest.mark.parametrize("N", [1, 2, 31, 63, 64, 65, 96, 127, 128, 129, 130, 192, 256, 257])
 def test_lengths(orc, N):
     run_full(orc, 1, 2, N, 128, N % 2 == 1, seed=N)
 
