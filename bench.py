@@ -69,11 +69,36 @@ def decode_bytes(B, Hq, Hkv, L, d, esize=2):
     return 2 * B * Hkv * L * d * esize + B * Hq * d * esize + B * Hq * d * 4
 
 
+def code_text(src):
+    """A source with its comments removed and its whitespace collapsed: what
+    the compiler sees, so that editing a comment keeps the digest."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif src[i] == '"':
+            j = i + 1
+            while j < n and src[j] != '"':
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(src[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest(*names):
+    """Digest of the code (comments and layout excluded) of kernel sources."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "flashattention_attention_fa_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "flashattention_attention_fa_amd", "csrc", n), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -44,8 +44,8 @@
 //                 LDS read.
 // The 16x16x32 product reads and writes a quarter of the accumulator per
 // instruction that the 32x32x16 one does, for half its work: measured alone
-// on MI355X, under the board's power limit, it sustains 6 % more fp16 and
-// 3 % more bf16 throughput, and the forward follows.
+// on MI355X (two boxes), under the board's power limit, it sustains 9-12 %
+// more fp16 and 2-6 % more bf16 throughput, and the forward follows.
 // Epilogue: O /= l, lse = (m + log2 l) * ln 2, both fp32.  With bf16 weights
 //                 O is divided by l plus a correction that swaps in the
 //                 rounded weights of tiles that could dominate the row (see

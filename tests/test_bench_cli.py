@@ -127,3 +127,16 @@ def test_check_heads_measures_every_row():
     assert abs(res["max_abs"] - 0.01) < 1e-5
     assert abs(res["lse_max_abs"] - 0.002) < 1e-5
     assert res["worst_row"] == (0, 1, 17)
+
+
+def test_source_digest_ignores_comments_and_layout():
+    """The traffic record of a kernel stays valid across comment edits: the
+    digest covers the code only, string literals included."""
+    import bench
+    a = bench.code_text('int f(int x) {  // first\n  return x + 1; /* two\nlines */ }\n')
+    b = bench.code_text('/* header */ int f(int x)\n{\n  return x + 1;\n}  // tail\n')
+    assert a == b == "int f(int x) { return x + 1; }"
+    assert bench.code_text('s = "a//b /* c */"; // x') == 's = "a//b /* c */";'
+    assert bench.code_text('int x = 1;') != bench.code_text('int x = 2;')
+    d = bench.source_digest("fa_fwd.hip", "fa_device.hpp")
+    assert len(d) == 16 and d == bench.source_digest("fa_fwd.hip", "fa_device.hpp")
